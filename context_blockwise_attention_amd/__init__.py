@@ -1,0 +1,256 @@
+"""Blockwise (ring / context-parallel) attention on AMD gfx950.
+
+A thin ctypes binding over ``libcpattn.so`` (C ABI in ``include/cpattn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments: it turns torch tensors into (pointer, sizes, strides)
+descriptors and passes the current HIP stream.  PyTorch supplies device
+memory and streams, nothing else.  There is no fallback: if the library is
+missing or a call is rejected, an exception says why.
+
+Entry points (same names as the C ABI):
+
+* :class:`Mask` -- ``Mask.causal(n_pos)`` / ``Mask.tree(seg_id, parent)``:
+  visibility descriptors.
+* :func:`partial` -- (O, LSE) of a query block against one K/V block,
+  optionally merged into a running (O, LSE).
+* :func:`merge` -- merge of several partials.
+* :func:`ring_emulate` -- every round of a ring of N ranks on one GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EDEVICE, ENOMEM = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("cpattn error %d: %s" % (code, msg))
+        self.code = code
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_heads", ctypes.c_int64), ("n_tok", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64), ("stride_tok", ctypes.c_int64)]
+
+
+class _PosMap(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_int64), ("stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libcpattn.so is not built: run `python -m context_blockwise_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.cpattn_last_error.restype = ctypes.c_char_p
+        L.cpattn_version.restype = ctypes.c_int
+        L.cpattn_mask_causal.argtypes = [ctypes.c_int64, ctypes.POINTER(P)]
+        L.cpattn_mask_tree.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, P, ctypes.POINTER(P)]
+        L.cpattn_mask_free.argtypes = [P]
+        L.cpattn_mask_npos.argtypes = [P]
+        L.cpattn_mask_npos.restype = ctypes.c_int64
+        L.cpattn_partial.argtypes = [ctypes.POINTER(_Tensor)] * 3 + [P, _PosMap, _PosMap, ctypes.c_float,
+                                                                      P, P, ctypes.c_int, P]
+        L.cpattn_merge.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int64, P, P, P]
+        L.cpattn_ring_emulate.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float,
+                                          P, P, P]
+        for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
+                  "cpattn_merge", "cpattn_ring_emulate"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise CpattnError(rc, lib().cpattn_last_error().decode())
+
+
+def version() -> Tuple[int, int]:
+    v = lib().cpattn_version()
+    return v >> 16, v & 0xFFFF
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _desc(t: Optional[torch.Tensor], name: str) -> _Tensor:
+    if t is None:
+        return _Tensor(None, BF16, 0, 1, 0, 64, 64, 64)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dim() != 3:
+        raise ValueError("%s must be [heads, tokens, d]" % name)
+    if t.dtype == torch.bfloat16:
+        dt = BF16
+    elif t.dtype == torch.float32:
+        dt = F32
+    else:
+        raise CpattnError(EUNSUPPORTED, "%s dtype %s unsupported (bf16 or f32)" % (name, t.dtype))
+    if t.stride(2) != 1:
+        raise CpattnError(EUNSUPPORTED, "%s: the last dimension must be contiguous" % name)
+    H, n, d = t.shape
+    return _Tensor(t.data_ptr(), dt, 0, H, n, d, t.stride(0), t.stride(1))
+
+
+def _posmap(p) -> _PosMap:
+    if p is None:
+        return _PosMap(0, 1)
+    base, stride = p
+    return _PosMap(int(base), int(stride))
+
+
+class Mask:
+    """Visibility descriptor.  Key position x is visible to query position y
+    iff x <= y < end[x]; end[x] = +inf for a causal mask, and the end of the
+    subtree of x's segment for a prefix tree stored in depth-first preorder."""
+
+    def __init__(self, handle: int, n_pos: int, kind: str):
+        self._h = ctypes.c_void_p(handle)
+        self.n_pos = n_pos
+        self.kind = kind
+
+    @classmethod
+    def causal(cls, n_pos: int) -> "Mask":
+        h = ctypes.c_void_p()
+        _check(lib().cpattn_mask_causal(int(n_pos), ctypes.byref(h)))
+        return cls(h.value, int(n_pos), "causal")
+
+    @classmethod
+    def tree(cls, seg_id, parent, stream=None) -> "Mask":
+        import numpy as np
+        seg = np.ascontiguousarray(seg_id, dtype=np.int32)
+        par = np.ascontiguousarray(parent, dtype=np.int32)
+        h = ctypes.c_void_p()
+        _check(lib().cpattn_mask_tree(seg.ctypes.data, seg.shape[0], par.ctypes.data, par.shape[0],
+                                      _stream(stream), ctypes.byref(h)))
+        return cls(h.value, int(seg.shape[0]), "tree")
+
+    @property
+    def handle(self):
+        if self._h is None or not self._h.value:
+            raise ValueError("mask already freed")
+        return self._h
+
+    def free(self):
+        if self._h is not None and self._h.value:
+            _check(lib().cpattn_mask_free(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            if _lib is not None and self._h is not None and self._h.value:
+                _lib.cpattn_mask_free(self._h)
+        except Exception:
+            pass
+
+
+def _default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, q_pos=(0, 1), k_pos=(0, 1),
+            scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+            accumulate: bool = False, stream=None):
+    """(O [H, n_q, d] fp32, LSE [H, n_q] fp32) of ``q`` against the block
+    ``k``/``v``.  Positions: row i of the query block sits at
+    ``q_pos[0] + q_pos[1] * i`` (likewise ``k_pos``).  With ``accumulate``
+    the result is merged into ``out`` (which must hold a running result)."""
+    H, nq, d = q.shape
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out=")
+        out = (torch.empty((H, nq, d), dtype=torch.float32, device=q.device),
+               torch.empty((H, nq), dtype=torch.float32, device=q.device))
+    o, lse = out
+    if o.shape != (H, nq, d) or lse.shape != (H, nq) or o.dtype != torch.float32 or lse.dtype != torch.float32 \
+            or not o.is_contiguous() or not lse.is_contiguous():
+        raise ValueError("out must be contiguous fp32 ([H, n_q, d], [H, n_q])")
+    qd, kd, vd = _desc(q, "q"), _desc(k, "k"), _desc(v, "v")
+    _check(lib().cpattn_partial(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), mask.handle,
+                                _posmap(q_pos), _posmap(k_pos),
+                                float(_default_scale(d) if scale is None else scale),
+                                o.data_ptr(), lse.data_ptr(), 1 if accumulate else 0, _stream(stream)))
+    return o, lse
+
+
+def merge(parts: Sequence[Tuple[torch.Tensor, torch.Tensor]], out=None, stream=None):
+    """Merge of partials ``[(O_p, LSE_p), ...]`` (fp32, O_p [..., d],
+    LSE_p [...]) into one (O, LSE)."""
+    parts = list(parts)
+    if not parts:
+        raise ValueError("nothing to merge")
+    o0, l0 = parts[0]
+    d = o0.shape[-1]
+    rows = l0.numel()
+    for o, l in parts:
+        if o.shape != o0.shape or l.shape != l0.shape or o.dtype != torch.float32 or l.dtype != torch.float32 \
+                or not o.is_contiguous() or not l.is_contiguous() or not o.is_cuda:
+            raise ValueError("parts must be contiguous fp32 device tensors of one shape")
+        if o.numel() != rows * d:
+            raise ValueError("O and LSE shapes disagree")
+    if out is None:
+        out = (torch.empty_like(o0), torch.empty_like(l0))
+    n = len(parts)
+    optrs = (ctypes.c_void_p * n)(*[p[0].data_ptr() for p in parts])
+    lptrs = (ctypes.c_void_p * n)(*[p[1].data_ptr() for p in parts])
+    _check(lib().cpattn_merge(n, optrs, lptrs, rows, d, out[0].data_ptr(), out[1].data_ptr(), _stream(stream)))
+    return out
+
+
+def ring_emulate(q_blocks: Sequence[Optional[torch.Tensor]], k_blocks: Sequence[torch.Tensor],
+                 v_blocks: Sequence[torch.Tensor], pos: Sequence[Tuple[int, int]], mask: Mask,
+                 scale: Optional[float] = None, ranks: Optional[Sequence[int]] = None, outs=None, stream=None):
+    """Ring attention of N emulated ranks on one GPU.  Rank r holds
+    ``q_blocks[r]``, ``k_blocks[r]``, ``v_blocks[r]`` at positions
+    ``pos[r] = (base, stride)``; in round k it visits the K/V of rank
+    ``(r - k) mod N``.  Returns ``{rank: (O, LSE)}`` for the ranks run."""
+    N = len(k_blocks)
+    if not (len(v_blocks) == len(pos) == len(q_blocks) == N):
+        raise ValueError("every rank needs a q/k/v block and positions")
+    run = list(range(N)) if ranks is None else [int(r) for r in ranks]
+    d = k_blocks[0].shape[2]
+    H = k_blocks[0].shape[0]
+    if outs is None:
+        outs = {}
+        for r in run:
+            nq = q_blocks[r].shape[1]
+            outs[r] = (torch.empty((H, nq, d), dtype=torch.float32, device=k_blocks[0].device),
+                       torch.empty((H, nq), dtype=torch.float32, device=k_blocks[0].device))
+    for r in run:
+        o, l = outs[r]
+        nq = q_blocks[r].shape[1]
+        if o.shape != (H, nq, d) or l.shape != (H, nq) or o.dtype != torch.float32 or l.dtype != torch.float32 \
+                or not o.is_contiguous() or not l.is_contiguous():
+            raise ValueError("outs[%d] must be contiguous fp32 ([H, n_q, d], [H, n_q])" % r)
+    qd = (_Tensor * N)(*[_desc(q_blocks[r] if r in run else None, "q") for r in range(N)])
+    kd = (_Tensor * N)(*[_desc(k, "k") for k in k_blocks])
+    vd = (_Tensor * N)(*[_desc(v, "v") for v in v_blocks])
+    pd = (_PosMap * N)(*[_posmap(p) for p in pos])
+    rk = (ctypes.c_int * len(run))(*run)
+    op = (ctypes.c_void_p * N)(*[(outs[r][0].data_ptr() if r in outs else None) for r in range(N)])
+    lp = (ctypes.c_void_p * N)(*[(outs[r][1].data_ptr() if r in outs else None) for r in range(N)])
+    _check(lib().cpattn_ring_emulate(N, qd, kd, vd, pd, rk, len(run), mask.handle,
+                                     float(_default_scale(d) if scale is None else scale), op, lp,
+                                     _stream(stream)))
+    return {r: outs[r] for r in run}

@@ -1,0 +1,492 @@
+// api.hip -- C ABI of the blockwise attention library (declared in cpattn.h).
+//
+// Host responsibilities: argument validation (fail fast, no fallback), the
+// prefix-tree visibility descriptor, the ring schedule (which key/value block
+// each rank visits in each round, which rounds are empty), and packing the
+// work of one round into a single launch.  All arithmetic runs in the kernels
+// of attn_kernel.hpp and merge_kernel.hpp.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cpattn.h"
+#include "attn_kernel.hpp"
+#include "merge_kernel.hpp"
+
+using namespace cpattn;
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local std::string g_last_error;
+
+static int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+static int hip_fail(hipError_t e, const char* what) {
+    return fail(CPATTN_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+extern "C" const char* cpattn_last_error(void) { return g_last_error.c_str(); }
+extern "C" int cpattn_version(void) { return (CPATTN_VERSION_MAJOR << 16) | CPATTN_VERSION_MINOR; }
+
+// ---------------------------------------------------------------------------
+// visibility descriptor
+// ---------------------------------------------------------------------------
+struct SegInfo {
+    int32_t run_start, run_end, parent, subtree_end;
+};
+
+struct cpattn_mask {
+    int32_t kind;                 // kCausal or kTree
+    int64_t n_pos;
+    std::vector<SegInfo> segs;    // host copy (tree)
+    int32_t* d_seg = nullptr;     // [n_pos]
+    int32_t* d_end = nullptr;     // [n_pos]
+    int4* d_segtab = nullptr;     // [n_seg]
+};
+
+extern "C" int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out) {
+    if (!out) return fail(CPATTN_EINVAL, "cpattn_mask_causal: out is NULL");
+    if (n_pos < 0 || n_pos > INT32_MAX) return fail(CPATTN_EINVAL, "cpattn_mask_causal: n_pos %lld out of range", (long long)n_pos);
+    cpattn_mask* m = new (std::nothrow) cpattn_mask();
+    if (!m) return fail(CPATTN_ENOMEM, "cpattn_mask_causal: out of host memory");
+    m->kind = kCausal;
+    m->n_pos = n_pos;
+    *out = m;
+    return CPATTN_OK;
+}
+
+extern "C" int cpattn_mask_free(cpattn_mask* m) {
+    if (!m) return CPATTN_OK;
+    hipError_t e1 = m->d_seg ? hipFree(m->d_seg) : hipSuccess;
+    hipError_t e2 = m->d_end ? hipFree(m->d_end) : hipSuccess;
+    hipError_t e3 = m->d_segtab ? hipFree(m->d_segtab) : hipSuccess;
+    delete m;
+    if (e1 != hipSuccess) return hip_fail(e1, "cpattn_mask_free");
+    if (e2 != hipSuccess) return hip_fail(e2, "cpattn_mask_free");
+    if (e3 != hipSuccess) return hip_fail(e3, "cpattn_mask_free");
+    return CPATTN_OK;
+}
+
+extern "C" int64_t cpattn_mask_npos(const cpattn_mask* m) { return m ? m->n_pos : -1; }
+
+// Builds the horizon representation of a prefix tree stored in depth-first
+// preorder: for each segment its run [run_start, run_end), its parent and the
+// end of its subtree; for each position its segment and subtree end.
+extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
+                                void* stream, cpattn_mask** out) {
+    if (!out) return fail(CPATTN_EINVAL, "cpattn_mask_tree: out is NULL");
+    *out = nullptr;
+    if (n_tok < 0 || n_tok > INT32_MAX) return fail(CPATTN_EINVAL, "cpattn_mask_tree: n_tok %lld out of range", (long long)n_tok);
+    if (n_seg < 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: n_seg < 0");
+    if ((n_tok > 0 && !seg_id) || (n_seg > 0 && !parent)) return fail(CPATTN_EINVAL, "cpattn_mask_tree: NULL array");
+    if (n_tok > 0 && n_seg == 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: tokens but no segments");
+
+    std::vector<SegInfo> segs((size_t)n_seg, SegInfo{-1, -1, -1, -1});
+    for (int32_t s = 0; s < n_seg; ++s) {
+        if (parent[s] < -1 || parent[s] >= n_seg || parent[s] == s)
+            return fail(CPATTN_EINVAL, "cpattn_mask_tree: parent[%d] = %d out of range", s, parent[s]);
+        segs[s].parent = parent[s];
+    }
+    // runs: every segment must be one contiguous, non-empty run
+    std::vector<int32_t> order;   // segments in storage order
+    for (int64_t x = 0; x < n_tok; ++x) {
+        int32_t s = seg_id[x];
+        if (s < 0 || s >= n_seg) return fail(CPATTN_EINVAL, "cpattn_mask_tree: seg_id[%lld] = %d out of range", (long long)x, s);
+        if (x == 0 || seg_id[x - 1] != s) {
+            if (segs[s].run_start >= 0)
+                return fail(CPATTN_EINVAL, "cpattn_mask_tree: segment %d is split into several runs", s);
+            segs[s].run_start = (int32_t)x;
+            order.push_back(s);
+        }
+        segs[s].run_end = (int32_t)x + 1;
+    }
+    for (int32_t s = 0; s < n_seg; ++s)
+        if (segs[s].run_start < 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: segment %d has no token", s);
+    // cycles (a parent chain that never reaches a root)
+    for (int32_t s = 0; s < n_seg; ++s) {
+        int32_t cur = s;
+        int32_t steps = 0;
+        while (cur >= 0 && steps <= n_seg) { cur = segs[cur].parent; ++steps; }
+        if (cur >= 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: parent links of segment %d form a cycle", s);
+    }
+    // depth-first preorder: walking segments in storage order, the parent of
+    // each must be on the stack of open ancestors; a segment's subtree closes
+    // when a segment that is not its descendant starts.
+    std::vector<int32_t> stack;
+    for (size_t i = 0; i < order.size(); ++i) {
+        int32_t s = order[i];
+        int32_t p = segs[s].parent;
+        while (!stack.empty() && stack.back() != p) {
+            segs[stack.back()].subtree_end = segs[s].run_start;
+            stack.pop_back();
+        }
+        if (p >= 0 && stack.empty())
+            return fail(CPATTN_EUNSUPPORTED,
+                        "cpattn_mask_tree: segment %d is not stored inside its parent %d's subtree "
+                        "(the row must be in depth-first preorder)", s, p);
+        stack.push_back(s);
+    }
+    while (!stack.empty()) {
+        segs[stack.back()].subtree_end = (int32_t)n_tok;
+        stack.pop_back();
+    }
+
+    cpattn_mask* m = new (std::nothrow) cpattn_mask();
+    if (!m) return fail(CPATTN_ENOMEM, "cpattn_mask_tree: out of host memory");
+    m->kind = kTree;
+    m->n_pos = n_tok;
+    m->segs = segs;
+    std::vector<int32_t> end((size_t)n_tok);
+    for (int64_t x = 0; x < n_tok; ++x) end[x] = segs[seg_id[x]].subtree_end;
+    std::vector<int4> tab((size_t)n_seg);
+    for (int32_t s = 0; s < n_seg; ++s)
+        tab[s] = int4{segs[s].run_start, segs[s].run_end, segs[s].parent, segs[s].subtree_end};
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    size_t nb = sizeof(int32_t) * (size_t)std::max<int64_t>(n_tok, 1);
+    size_t tb = sizeof(int4) * (size_t)std::max<int32_t>(n_seg, 1);
+    hipError_t e;
+    if ((e = hipMalloc(&m->d_seg, nb)) != hipSuccess || (e = hipMalloc(&m->d_end, nb)) != hipSuccess ||
+        (e = hipMalloc(&m->d_segtab, tb)) != hipSuccess) {
+        cpattn_mask_free(m);
+        return fail(CPATTN_ENOMEM, "cpattn_mask_tree: hipMalloc: %s", hipGetErrorString(e));
+    }
+    if (n_tok > 0) {
+        if ((e = hipMemcpyAsync(m->d_seg, seg_id, sizeof(int32_t) * n_tok, hipMemcpyHostToDevice, st)) != hipSuccess ||
+            (e = hipMemcpyAsync(m->d_end, end.data(), sizeof(int32_t) * n_tok, hipMemcpyHostToDevice, st)) != hipSuccess) {
+            cpattn_mask_free(m);
+            return hip_fail(e, "cpattn_mask_tree: upload");
+        }
+    }
+    if (n_seg > 0 &&
+        (e = hipMemcpyAsync(m->d_segtab, tab.data(), sizeof(int4) * n_seg, hipMemcpyHostToDevice, st)) != hipSuccess) {
+        cpattn_mask_free(m);
+        return hip_fail(e, "cpattn_mask_tree: upload");
+    }
+    // the host staging vectors die with this call
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) {
+        cpattn_mask_free(m);
+        return hip_fail(e, "cpattn_mask_tree: upload");
+    }
+    *out = m;
+    return CPATTN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// argument checks
+// ---------------------------------------------------------------------------
+static int check_tensor(const cpattn_tensor* t, const char* who, const char* name) {
+    if (!t) return fail(CPATTN_EINVAL, "%s: %s is NULL", who, name);
+    if (t->dtype != CPATTN_BF16 && t->dtype != CPATTN_F32)
+        return fail(CPATTN_EUNSUPPORTED, "%s: %s dtype %d unsupported (bf16 or f32)", who, name, t->dtype);
+    if (t->d != 64 && t->d != 128)
+        return fail(CPATTN_EUNSUPPORTED, "%s: %s head dim %lld unsupported (64 or 128)", who, name, (long long)t->d);
+    if (t->n_heads < 1 || t->n_tok < 0 || t->n_tok > INT32_MAX)
+        return fail(CPATTN_EINVAL, "%s: %s has bad sizes (heads %lld, tokens %lld)", who, name,
+                    (long long)t->n_heads, (long long)t->n_tok);
+    const int64_t al = t->dtype == CPATTN_BF16 ? 8 : 4;
+    if (t->n_tok > 0 && !t->data) return fail(CPATTN_EINVAL, "%s: %s data is NULL", who, name);
+    if ((reinterpret_cast<uintptr_t>(t->data) & 15) != 0)
+        return fail(CPATTN_EUNSUPPORTED, "%s: %s data is not 16-byte aligned", who, name);
+    if (t->stride_tok % al != 0 || t->stride_head % al != 0 || t->stride_tok < t->d || t->stride_head < 0)
+        return fail(CPATTN_EUNSUPPORTED, "%s: %s strides (%lld, %lld) unsupported", who, name,
+                    (long long)t->stride_head, (long long)t->stride_tok);
+    return CPATTN_OK;
+}
+
+static int check_posmap(cpattn_posmap p, int64_t n, const cpattn_mask* m, const char* who, const char* name) {
+    if (p.stride < 1) return fail(CPATTN_EINVAL, "%s: %s stride %lld < 1", who, name, (long long)p.stride);
+    if (n == 0) return CPATTN_OK;
+    const int64_t last = p.base + p.stride * (n - 1);
+    if (p.base < 0 || last >= m->n_pos || last < p.base)
+        return fail(CPATTN_EINVAL, "%s: %s positions [%lld, %lld] outside the mask's [0, %lld)", who, name,
+                    (long long)p.base, (long long)last, (long long)m->n_pos);
+    return CPATTN_OK;
+}
+
+// Does any query of the block see any key of the block?  Exact for both masks
+// (per segment, the smallest key position gives the widest chance).
+static bool pair_nonempty(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
+    if (nq == 0 || nk == 0) return false;
+    const int64_t qmax = qp.base + qp.stride * (nq - 1);
+    auto first_query_at_or_after = [&](int64_t x) -> int64_t {
+        if (x <= qp.base) return qp.base;
+        int64_t i = (x - qp.base + qp.stride - 1) / qp.stride;
+        return qp.base + qp.stride * i;
+    };
+    if (m->kind == kCausal) return kp.base <= qmax;
+    const int64_t kmax = kp.base + kp.stride * (nk - 1);
+    for (const SegInfo& s : m->segs) {
+        int64_t lo = std::max<int64_t>(s.run_start, kp.base);
+        int64_t hi = std::min<int64_t>(s.run_end - 1, kmax);
+        if (lo > hi) continue;
+        int64_t j = (lo - kp.base + kp.stride - 1) / kp.stride;   // first key of the block in the run
+        int64_t xa = kp.base + kp.stride * j;
+        if (xa > hi) continue;
+        int64_t y = first_query_at_or_after(xa);
+        if (y <= qmax && y < s.subtree_end) return true;
+    }
+    return false;
+}
+
+// ---------------------------------------------------------------------------
+// launches
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BN>
+static int launch_partial_t(LaunchArgs& a, hipStream_t st) {
+    using TL = Tile<T, D, BN>;
+    const int smem = 2 * TL::STAGE_BYTES;
+    static bool attr_set = false;   // per instantiation; the attribute is per function
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&partial_attention_kernel<T, D, BN>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        attr_set = true;
+    }
+    const int grid = (a.total_wg + 7) / 8 * 8;
+    hipLaunchKernelGGL((partial_attention_kernel<T, D, BN>), dim3(grid), dim3(kThreads), smem, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "partial attention launch");
+    return CPATTN_OK;
+}
+
+static int launch_partial(LaunchArgs& a, int dtype, int d, hipStream_t st) {
+    if (a.total_wg == 0) return CPATTN_OK;
+    if (dtype == CPATTN_BF16) {
+        if (d == 128) return launch_partial_t<__bf16, 128, 64>(a, st);
+        return launch_partial_t<__bf16, 64, 64>(a, st);
+    }
+    if (d == 128) return launch_partial_t<float, 128, 32>(a, st);
+    return launch_partial_t<float, 64, 32>(a, st);
+}
+
+static MaskArgs mask_args(const cpattn_mask* m) {
+    MaskArgs ma{};
+    ma.kind = m->kind;
+    ma.n_pos = m->n_pos;
+    ma.seg = m->d_seg;
+    ma.end = m->d_end;
+    ma.segtab = m->d_segtab;
+    ma.n_seg = (int32_t)m->segs.size();
+    return ma;
+}
+
+static JobArgs make_job(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, cpattn_posmap qp,
+                        cpattn_posmap kp, float* o, float* lse, int accumulate) {
+    JobArgs j{};
+    j.q = q->data;
+    j.k = k->data;
+    j.v = v->data;
+    j.o = o;
+    j.lse = lse;
+    j.q_sh = q->stride_head;
+    j.q_st = q->stride_tok;
+    j.k_sh = k->stride_head;
+    j.k_st = k->stride_tok;
+    j.v_sh = v->stride_head;
+    j.v_st = v->stride_tok;
+    j.qbase = qp.base;
+    j.qstride = qp.stride;
+    j.kbase = kp.base;
+    j.kstride = kp.stride;
+    j.n_q = (int32_t)q->n_tok;
+    j.n_k = (int32_t)k->n_tok;
+    j.accumulate = accumulate;
+    j.q_tiles = (int32_t)((q->n_tok + kBM - 1) / kBM);
+    return j;
+}
+
+// Packs jobs into launches of at most kMaxJobs each.
+static int run_jobs(std::vector<JobArgs>& jobs, const cpattn_mask* m, int heads, float scale, int dtype, int d,
+                    hipStream_t st) {
+    const float scale_log2 = scale * 1.4426950408889634f;
+    for (size_t first = 0; first < jobs.size(); first += kMaxJobs) {
+        LaunchArgs a{};
+        a.mask = mask_args(m);
+        a.heads = heads;
+        a.scale_log2 = scale_log2;
+        int64_t total = 0;
+        int n = 0;
+        for (size_t i = first; i < jobs.size() && n < kMaxJobs; ++i, ++n) {
+            a.jobs[n] = jobs[i];
+            a.jobs[n].wg_begin = (int32_t)total;
+            total += (int64_t)jobs[i].q_tiles * heads;
+        }
+        if (total > INT32_MAX / 2) return fail(CPATTN_EUNSUPPORTED, "too many workgroups in one launch");
+        a.n_jobs = n;
+        a.total_wg = (int32_t)total;
+        int rc = launch_partial(a, dtype, d, st);
+        if (rc != CPATTN_OK) return rc;
+    }
+    return CPATTN_OK;
+}
+
+static int launch_fill(float* o, float* lse, int64_t rows, int64_t d, hipStream_t st) {
+    if (rows == 0) return CPATTN_OK;
+    const int64_t n = rows * d;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_empty_kernel, dim3((unsigned)blocks), dim3(256), 0, st, o, lse, rows, d);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "fill launch");
+}
+
+static int check_qkv(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, const char* who) {
+    int rc;
+    if ((rc = check_tensor(q, who, "q")) || (rc = check_tensor(k, who, "k")) || (rc = check_tensor(v, who, "v"))) return rc;
+    if (q->dtype != k->dtype || q->dtype != v->dtype)
+        return fail(CPATTN_EUNSUPPORTED, "%s: q, k and v must share one dtype", who);
+    if (q->d != k->d || q->d != v->d) return fail(CPATTN_EUNSUPPORTED, "%s: q, k and v must share one head dim", who);
+    if (q->n_heads != k->n_heads || q->n_heads != v->n_heads)
+        return fail(CPATTN_EINVAL, "%s: head counts differ (q %lld, k %lld, v %lld)", who, (long long)q->n_heads,
+                    (long long)k->n_heads, (long long)v->n_heads);
+    if (k->n_tok != v->n_tok) return fail(CPATTN_EINVAL, "%s: k and v token counts differ", who);
+    return CPATTN_OK;
+}
+
+static int check_scale(float scale, const char* who) {
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(CPATTN_EUNSUPPORTED, "%s: scale must be finite and > 0", who);
+    return CPATTN_OK;
+}
+
+static int check_out(const float* o, const float* lse, const char* who) {
+    if (!o || !lse) return fail(CPATTN_EINVAL, "%s: output pointer is NULL", who);
+    if ((reinterpret_cast<uintptr_t>(o) & 15) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3) != 0)
+        return fail(CPATTN_EUNSUPPORTED, "%s: o must be 16-byte aligned and lse 4-byte aligned", who);
+    return CPATTN_OK;
+}
+
+extern "C" int cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                              const cpattn_mask* mask, cpattn_posmap q_pos, cpattn_posmap k_pos, float scale,
+                              float* o_out, float* lse_out, int accumulate, void* stream) {
+    const char* who = "cpattn_partial";
+    int rc;
+    if ((rc = check_qkv(q, k, v, who))) return rc;
+    if (!mask) return fail(CPATTN_EINVAL, "%s: mask is NULL", who);
+    if ((rc = check_scale(scale, who))) return rc;
+    if (accumulate != 0 && accumulate != 1) return fail(CPATTN_EINVAL, "%s: accumulate must be 0 or 1", who);
+    if (q->n_tok == 0) return CPATTN_OK;
+    if ((rc = check_out(o_out, lse_out, who))) return rc;
+    if ((rc = check_posmap(q_pos, q->n_tok, mask, who, "q_pos")) || (rc = check_posmap(k_pos, k->n_tok, mask, who, "k_pos")))
+        return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (k->n_tok == 0 || !pair_nonempty(mask, q_pos, q->n_tok, k_pos, k->n_tok)) {
+        if (accumulate) return CPATTN_OK;   // merging an empty partial is the identity
+        return launch_fill(o_out, lse_out, q->n_heads * q->n_tok, q->d, st);
+    }
+    std::vector<JobArgs> jobs{make_job(q, k, v, q_pos, k_pos, o_out, lse_out, accumulate)};
+    return run_jobs(jobs, mask, (int)q->n_heads, scale, q->dtype, (int)q->d, st);
+}
+
+extern "C" int cpattn_ring_emulate(int N, const cpattn_tensor* q_blocks, const cpattn_tensor* k_blocks,
+                                   const cpattn_tensor* v_blocks, const cpattn_posmap* pos, const int* ranks,
+                                   int n_ranks_run, const cpattn_mask* mask, float scale, float* const* o_out,
+                                   float* const* lse_out, void* stream) {
+    const char* who = "cpattn_ring_emulate";
+    int rc;
+    if (N < 1 || N > 64) return fail(CPATTN_EINVAL, "%s: N = %d out of range [1, 64]", who, N);
+    if (!q_blocks || !k_blocks || !v_blocks || !pos || !o_out || !lse_out)
+        return fail(CPATTN_EINVAL, "%s: NULL array argument", who);
+    if (!mask) return fail(CPATTN_EINVAL, "%s: mask is NULL", who);
+    if ((rc = check_scale(scale, who))) return rc;
+    std::vector<int> run;
+    if (!ranks) {
+        if (n_ranks_run != N) return fail(CPATTN_EINVAL, "%s: ranks is NULL but n_ranks_run != N", who);
+        for (int r = 0; r < N; ++r) run.push_back(r);
+    } else {
+        if (n_ranks_run < 0 || n_ranks_run > N) return fail(CPATTN_EINVAL, "%s: n_ranks_run out of range", who);
+        std::vector<char> seen(N, 0);
+        for (int i = 0; i < n_ranks_run; ++i) {
+            if (ranks[i] < 0 || ranks[i] >= N) return fail(CPATTN_EINVAL, "%s: rank %d out of range", who, ranks[i]);
+            if (seen[ranks[i]]) return fail(CPATTN_EINVAL, "%s: rank %d listed twice", who, ranks[i]);
+            seen[ranks[i]] = 1;
+            run.push_back(ranks[i]);
+        }
+    }
+    // every rank's K/V block is visited; only the ranks that run need queries
+    const cpattn_tensor& ref = k_blocks[0];
+    for (int r = 0; r < N; ++r) {
+        if ((rc = check_qkv(&k_blocks[r], &k_blocks[r], &v_blocks[r], who))) return rc;
+        if (k_blocks[r].dtype != ref.dtype || k_blocks[r].d != ref.d || k_blocks[r].n_heads != ref.n_heads)
+            return fail(CPATTN_EUNSUPPORTED, "%s: every block must share dtype, head dim and heads", who);
+        if ((rc = check_posmap(pos[r], k_blocks[r].n_tok, mask, who, "pos"))) return rc;
+    }
+    for (int r : run) {
+        if ((rc = check_qkv(&q_blocks[r], &k_blocks[r], &v_blocks[r], who))) return rc;
+        if (q_blocks[r].n_tok != k_blocks[r].n_tok)
+            return fail(CPATTN_EINVAL, "%s: rank %d holds %lld queries but %lld keys at the same positions", who, r,
+                        (long long)q_blocks[r].n_tok, (long long)k_blocks[r].n_tok);
+        if (q_blocks[r].n_tok > 0 && (rc = check_out(o_out[r], lse_out[r], who))) return rc;
+    }
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int heads = (int)ref.n_heads;
+    const int dtype = ref.dtype;
+    const int d = (int)ref.d;
+    std::vector<char> written(N, 0);
+    for (int k = 0; k < N; ++k) {
+        std::vector<JobArgs> jobs;
+        for (int r : run) {
+            const int b = ((r - k) % N + N) % N;
+            if (!pair_nonempty(mask, pos[r], q_blocks[r].n_tok, pos[b], k_blocks[b].n_tok)) continue;
+            jobs.push_back(make_job(&q_blocks[r], &k_blocks[b], &v_blocks[b], pos[r], pos[b], o_out[r], lse_out[r],
+                                    written[r] ? 1 : 0));
+            written[r] = 1;
+        }
+        if ((rc = run_jobs(jobs, mask, heads, scale, dtype, d, st))) return rc;
+    }
+    for (int r : run)
+        if (!written[r] && (rc = launch_fill(o_out[r], lse_out[r], heads * q_blocks[r].n_tok, d, st))) return rc;
+    return CPATTN_OK;
+}
+
+extern "C" int cpattn_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts, int64_t n_rows,
+                            int64_t d, float* o_out, float* lse_out, void* stream) {
+    const char* who = "cpattn_merge";
+    if (n_parts < 1 || n_parts > kMaxMergeParts)
+        return fail(CPATTN_EINVAL, "%s: n_parts = %d out of range [1, %d]", who, n_parts, kMaxMergeParts);
+    if (n_rows < 0 || d < 1 || d > (1 << 20)) return fail(CPATTN_EINVAL, "%s: bad sizes", who);
+    if (!o_parts || !lse_parts) return fail(CPATTN_EINVAL, "%s: NULL part arrays", who);
+    if (n_rows == 0) return CPATTN_OK;
+    if (!o_out || !lse_out) return fail(CPATTN_EINVAL, "%s: NULL output", who);
+    MergeArgs a{};
+    const bool vec = d % 4 == 0 && (reinterpret_cast<uintptr_t>(o_out) & 15) == 0;
+    for (int p = 0; p < n_parts; ++p) {
+        if (!o_parts[p] || !lse_parts[p]) return fail(CPATTN_EINVAL, "%s: part %d is NULL", who, p);
+        a.o[p] = o_parts[p];
+        a.l[p] = lse_parts[p];
+    }
+    bool all_aligned = vec;
+    for (int p = 0; p < n_parts; ++p) all_aligned = all_aligned && (reinterpret_cast<uintptr_t>(o_parts[p]) & 15) == 0;
+    a.vec = all_aligned ? 4 : 1;
+    a.o_out = o_out;
+    a.l_out = lse_out;
+    a.rows = n_rows;
+    a.n = n_parts;
+    a.d = (int32_t)d;
+    const int64_t units = a.vec == 4 ? d / 4 : d;
+    a.tpr = (int32_t)std::min<int64_t>(256, std::max<int64_t>(1, units));
+    // round threads-per-row down to a divisor of 256 so rows never straddle workgroups
+    while (256 % a.tpr) --a.tpr;
+    const int64_t rows_per_block = 256 / a.tpr;
+    const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "merge launch");
+}

@@ -1,0 +1,170 @@
+/*
+ * cpattn.h -- blockwise (ring / context-parallel) attention for AMD gfx950.
+ *
+ * A query block computes a partial attention result against one visiting
+ * key/value block and returns it as the pair (O, LSE): the softmax-weighted
+ * sum of the visible values and the natural log of the softmax denominator
+ * over those keys ("Context Parallelism in ART", section 02, the attention
+ * definition and the LSE summary (o_A, L_A)).  Partials over disjoint key
+ * sets combine exactly with the log-sum-exp merge (same page, section 03),
+ * done here in fp32.  A ring of N ranks is emulated on one GPU by visiting,
+ * in round k, the key/value block of rank (r - k) mod N (ML-systems lesson on
+ * sequence/context parallelism, the ring-attention section).
+ *
+ * Conventions shared by every entry point:
+ *  - Status: every function returns CPATTN_OK (0) or a negative cpattn_status.
+ *    No exception crosses this interface.  cpattn_last_error() gives a message
+ *    for the calling thread's last failure.
+ *  - Memory: tensors, outputs and position data passed to compute calls are
+ *    device pointers owned by the caller, who keeps them alive until the
+ *    stream has finished with them.  The library allocates device memory only
+ *    inside mask descriptors (released by cpattn_mask_free).
+ *  - Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
+ *    Compute calls validate their arguments synchronously, then enqueue work
+ *    on the stream and return without waiting.  A launch failure returns
+ *    CPATTN_EDEVICE with the HIP error text.
+ *  - Fail fast: unsupported combinations return CPATTN_EUNSUPPORTED; nothing
+ *    falls back to another code path.
+ *  - Extents (token counts, head counts, block counts, tree shapes) are
+ *    runtime arguments; nothing recompiles when they change.
+ *  - Numerics: scores are accumulated in fp32 from bf16 or fp32 inputs, the
+ *    softmax runs in fp32, O and LSE are fp32, LSE is a natural log.  A row
+ *    that sees no key of the visiting block gets O = 0 and LSE = -inf (with
+ *    accumulate set, such a row keeps its running value).  NaN inputs
+ *    propagate.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPATTN_VERSION_MAJOR 0
+#define CPATTN_VERSION_MINOR 1
+
+typedef enum {
+    CPATTN_OK = 0,
+    CPATTN_EINVAL = -1,        /* malformed argument: sizes, ranks, tree links */
+    CPATTN_EUNSUPPORTED = -2,  /* well-formed but not implemented: dtype, head dim, layout */
+    CPATTN_EDEVICE = -3,       /* HIP runtime or launch failure */
+    CPATTN_ENOMEM = -4         /* device allocation failed (mask descriptors only) */
+} cpattn_status;
+
+typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
+
+/* A [n_heads][n_tok][d] tensor in device memory.  Element (h, i, c) lives at
+ * data + h*stride_head + i*stride_tok + c (strides in elements; the last
+ * dimension is contiguous).  `data` must be 16-byte aligned and both strides
+ * multiples of 8 elements (bf16) or 4 elements (f32). */
+typedef struct {
+    const void* data;
+    int32_t dtype;          /* cpattn_dtype */
+    int32_t reserved;
+    int64_t n_heads;
+    int64_t n_tok;
+    int64_t d;              /* head dimension: 64 or 128 */
+    int64_t stride_head;
+    int64_t stride_tok;
+} cpattn_tensor;
+
+/* Global position of row i of a block: base + stride * i (stride >= 1).
+ * Contiguous blocks use stride 1; the striped layout, where rank r holds the
+ * positions x with x % P == r (mstar PR 1141, the ring exchange), uses
+ * base = r, stride = P. */
+typedef struct {
+    int64_t base;
+    int64_t stride;
+} cpattn_posmap;
+
+/* Opaque visibility descriptor.  Immutable after creation; safe to share
+ * between calls and streams.  Visibility of key position x to query position
+ * y is "x <= y < end[x]", where end[x] is one past the last position of the
+ * subtree of x's segment (or +infinity for a causal mask). */
+typedef struct cpattn_mask cpattn_mask;
+
+/* Causal visibility over positions [0, n_pos): key x is visible to query y
+ * iff x <= y ("Context Parallelism in ART", section 02: a causal query reads
+ * positions up through its own).  Allocates no device memory.
+ * EINVAL if n_pos < 0 or out is NULL. */
+int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out);
+
+/* Prefix-tree visibility ("Context Parallelism in ART", section 02 and the
+ * tiny tree of section 03): a query sees the earlier-or-equal tokens of its
+ * own segment and every token of every strict ancestor segment.
+ *   seg_id[n_tok]: host array, segment of each physical position (0..n_seg-1);
+ *                  each segment must occupy one contiguous run.
+ *   parent[n_seg]: host array, parent segment (-1 for a root).
+ * The row must be stored in depth-first preorder: every segment's subtree
+ * occupies one contiguous range that starts with the segment itself (a
+ * parent precedes its children and no subtree is interleaved with another).
+ * Returns EUNSUPPORTED for a tree that is not stored that way, EINVAL for
+ * out-of-range ids, split segments or parent cycles, ENOMEM/EDEVICE on
+ * allocation or upload failure.  The upload is enqueued on `stream` and is
+ * complete when the function returns (the host arrays may be freed). */
+int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
+                     void* stream, cpattn_mask** out);
+
+/* Releases a descriptor and its device arrays.  The caller guarantees that no
+ * enqueued work still uses it.  NULL is accepted. */
+int cpattn_mask_free(cpattn_mask* m);
+
+/* Number of positions a descriptor covers (its n_pos / n_tok), or -1. */
+int64_t cpattn_mask_npos(const cpattn_mask* m);
+
+/* Partial attention of one query block against one key/value block.
+ *   q: [H][n_q][d], k and v: [H][n_k][d]; one dtype, one d, one H.
+ *   q_pos, k_pos: global positions of the rows (checked against the mask's
+ *                 n_pos: every row's position must lie in [0, n_pos)).
+ *   scale: multiplies q.k before the softmax (usually 1/sqrt(d)).
+ *   o: fp32, element (h, i, c) at o[h*o_stride_head + i*d + c]... see below.
+ *   o_out / lse_out: fp32 device arrays [H][n_q][d] and [H][n_q], contiguous.
+ *   accumulate = 0: write the partial (O, LSE).
+ *   accumulate = 1: read the running (O, LSE) already in o_out/lse_out and
+ *                   replace it by its merge with this partial, in fp32.
+ * Zero-sized blocks (n_q == 0 or n_k == 0) are a successful no-op when
+ * accumulate is set and write (0, -inf) rows otherwise. */
+int cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                   const cpattn_mask* mask, cpattn_posmap q_pos, cpattn_posmap k_pos, float scale,
+                   float* o_out, float* lse_out, int accumulate, void* stream);
+
+/* Merge of n_parts partial results ("Context Parallelism in ART", section 03,
+ * the stable form with m = max of the LSEs), all fp32 in device memory:
+ *   o_parts[p]: [n_rows][d], lse_parts[p]: [n_rows]   (n_rows = heads*rows)
+ *   o_out: [n_rows][d], lse_out: [n_rows]; may alias o_parts[0]/lse_parts[0].
+ * o_parts and lse_parts are HOST arrays of device pointers.  Rows whose
+ * every part has LSE = -inf give (0, -inf).  1 <= n_parts <= 64, d >= 1. */
+int cpattn_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
+                 int64_t n_rows, int64_t d, float* o_out, float* lse_out, void* stream);
+
+/* Ring emulation on one GPU.  N ranks each hold one query block q_blocks[r]
+ * and one key/value block (k_blocks[r], v_blocks[r]) with positions pos[r].
+ * For each rank r in ranks[0..n_ranks_run), every round k = 0..N-1 computes
+ * the partial of q_blocks[r] against the K/V block of rank (r - k) mod N and
+ * merges it into o_out[r]/lse_out[r] (round 0 writes, later rounds merge).
+ * Rounds in which no query of r sees any key of the visiting block are
+ * skipped (their merge would be the identity).  All ranks' round k run in
+ * one launch, as the ranks of a real ring run that round concurrently.
+ *   q_blocks, k_blocks, v_blocks, pos: host arrays of N entries.
+ *   o_out, lse_out: host arrays of N device pointers ([H][n_q_r][d] and
+ *                   [H][n_q_r] fp32); entries of ranks not run may be NULL.
+ *   ranks: host array of rank ids to run (NULL with n_ranks_run = N: all).
+ * 1 <= N <= 64. */
+int cpattn_ring_emulate(int N, const cpattn_tensor* q_blocks, const cpattn_tensor* k_blocks,
+                        const cpattn_tensor* v_blocks, const cpattn_posmap* pos,
+                        const int* ranks, int n_ranks_run, const cpattn_mask* mask, float scale,
+                        float* const* o_out, float* const* lse_out, void* stream);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* cpattn_last_error(void);
+
+/* (major << 16) | minor */
+int cpattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */
