@@ -206,6 +206,10 @@ static int check_tensor(const cpattn_tensor* t, const char* who, const char* nam
     if (t->stride_tok % al != 0 || t->stride_head % al != 0 || t->stride_tok < t->d || t->stride_head < 0)
         return fail(CPATTN_EUNSUPPORTED, "%s: %s strides (%lld, %lld) unsupported", who, name,
                     (long long)t->stride_head, (long long)t->stride_tok);
+    // the kernels address one head's rows with 32-bit byte offsets
+    const int64_t esize = t->dtype == CPATTN_BF16 ? 2 : 4;
+    if (t->n_tok > 0 && ((t->n_tok - 1) * t->stride_tok + t->d) * esize > INT32_MAX)
+        return fail(CPATTN_EUNSUPPORTED, "%s: %s spans more than 2 GiB per head", who, name);
     return CPATTN_OK;
 }
 
@@ -278,11 +282,10 @@ static int launch_partial(LaunchArgs& a, int dtype, int d, hipStream_t st) {
 static MaskArgs mask_args(const cpattn_mask* m) {
     MaskArgs ma{};
     ma.kind = m->kind;
-    ma.n_pos = m->n_pos;
+    ma.n_pos = (int32_t)m->n_pos;
     ma.seg = m->d_seg;
     ma.end = m->d_end;
     ma.segtab = m->d_segtab;
-    ma.n_seg = (int32_t)m->segs.size();
     return ma;
 }
 
@@ -295,15 +298,15 @@ static JobArgs make_job(const cpattn_tensor* q, const cpattn_tensor* k, const cp
     j.o = o;
     j.lse = lse;
     j.q_sh = q->stride_head;
-    j.q_st = q->stride_tok;
     j.k_sh = k->stride_head;
-    j.k_st = k->stride_tok;
     j.v_sh = v->stride_head;
-    j.v_st = v->stride_tok;
-    j.qbase = qp.base;
-    j.qstride = qp.stride;
-    j.kbase = kp.base;
-    j.kstride = kp.stride;
+    j.q_st = (int32_t)q->stride_tok;
+    j.k_st = (int32_t)k->stride_tok;
+    j.v_st = (int32_t)v->stride_tok;
+    j.qbase = (int32_t)qp.base;
+    j.qstride = (int32_t)qp.stride;
+    j.kbase = (int32_t)kp.base;
+    j.kstride = (int32_t)kp.stride;
     j.n_q = (int32_t)q->n_tok;
     j.n_k = (int32_t)k->n_tok;
     j.accumulate = accumulate;

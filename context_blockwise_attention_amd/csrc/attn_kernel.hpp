@@ -1,6 +1,6 @@
 // attn_kernel.hpp -- partial blockwise attention on gfx950 (CDNA4) MFMA.
 //
-// One workgroup = 4 waves = BM = 128 query rows of one head of one job; each
+// One workgroup = 4 waves = kBM = 128 query rows of one head of one job; each
 // wave owns 32 query rows.  The workgroup walks the key tiles (BN keys each)
 // that its queries can see, stages K and V^T in LDS (double buffered), and
 // keeps an online softmax per query row in registers ("Context Parallelism in
@@ -18,7 +18,15 @@
 //    MFMA (O^T += V^T P^T) wants as its B operand: P never leaves registers.
 //  * V is transposed while it is staged into LDS (V^T rows = head dims), so
 //    the A operand of O^T += V^T P^T is one 16-byte LDS read per lane.
-//  * O^T accumulators: lane l holds its query's 64 (D=128) output values.
+//  * O^T accumulators: lane l holds its query's D/2 output values.
+//  * The running max is only raised when a tile's max exceeds it by more than
+//    2^kTau (in the base-2 exponent), so the accumulator rescale -- a pass
+//    over every accumulator register -- is rare; probabilities stay below
+//    2^kTau, far inside fp32 and bf16 range, and the final normalisation uses
+//    the same stale max for numerator and denominator, so the result is the
+//    same softmax.
+//  * Global loads go through buffer resources: 32-bit offsets, and rows past
+//    the end of a block read as zero (those keys are masked out).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,7 +35,6 @@
 namespace cpattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -37,7 +44,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kMaxJobs = 16;
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kBM = 128;       // query rows per workgroup
-constexpr int kMaxTreeDepth = 1 << 20;
+constexpr float kTau = 8.0f;   // lazy-rescale threshold (base-2 exponent)
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit dwords (gfx9 family)
 
 enum MaskKind : int32_t { kCausal = 0, kTree = 1 };
 
@@ -48,22 +56,22 @@ struct JobArgs {
     const void* v;
     float* o;
     float* lse;
-    int64_t q_sh, q_st, k_sh, k_st, v_sh, v_st;  // element strides (head, token)
-    int64_t qbase, qstride, kbase, kstride;       // global positions of rows
+    int64_t q_sh, k_sh, v_sh;      // head strides (elements)
+    int32_t q_st, k_st, v_st;      // token strides (elements)
+    int32_t qbase, qstride;        // global position of query row i: qbase + qstride * i
+    int32_t kbase, kstride;        // same for key rows
     int32_t n_q, n_k;
     int32_t accumulate;
     int32_t q_tiles;   // ceil(n_q / kBM)
     int32_t wg_begin;  // first work item of this job
-    int32_t pad_;
 };
 
 struct MaskArgs {
     const int32_t* seg;     // [n_pos] segment of each position (tree only)
     const int4* segtab;     // [n_seg] {run_start, run_end, parent, subtree_end}
     const int32_t* end;     // [n_pos] subtree end of each position (tree only)
-    int64_t n_pos;
+    int32_t n_pos;
     int32_t kind;
-    int32_t n_seg;
 };
 
 struct LaunchArgs {
@@ -115,7 +123,8 @@ struct Tile {
     static constexpr int STAGE_BYTES = (K_ELEMS + V_ELEMS) * (int)sizeof(T) + BN * 4;
     static constexpr int K_CHUNKS = BN * D / EPC;            // 16-byte chunks of a K tile
     static constexpr int K_PER_THREAD = (K_CHUNKS + kThreads - 1) / kThreads;
-    static constexpr int V_GROUPS = (BN / 4) * (D / EPC);     // 4 keys x EPC dims each
+    static constexpr int KG = BN / 4;                          // 4-key groups of a V tile
+    static constexpr int V_GROUPS = KG * (D / EPC);            // 4 keys x EPC dims each
     static constexpr int V_PER_THREAD = (V_GROUPS + kThreads - 1) / kThreads;
     static constexpr int KB = BN / 32;                         // 32-key MFMA blocks per tile
     static constexpr int DSTEPS = D / 16;
@@ -125,12 +134,39 @@ struct Tile {
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// 8 consecutive elements as one MFMA operand (16-byte aligned source).
+// 8 consecutive elements as one MFMA operand (16-byte aligned LDS source).
 __device__ __forceinline__ bf16x8 load_op8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ f32x8 load_op8(const float* p) {
     f32x4 a = *reinterpret_cast<const f32x4*>(p);
     f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::op8 as_op8(u32x4 lo, u32x4 hi);
+template <>
+__device__ __forceinline__ bf16x8 as_op8<__bf16>(u32x4 lo, u32x4) { return __builtin_bit_cast(bf16x8, lo); }
+template <>
+__device__ __forceinline__ f32x8 as_op8<float>(u32x4 lo, u32x4 hi) {
+    f32x4 a = __builtin_bit_cast(f32x4, lo), b = __builtin_bit_cast(f32x4, hi);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// max / sum of a value with the same value of lane l ^ 32
+__device__ __forceinline__ float xhalf_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,7 +180,8 @@ __device__ __forceinline__ f32x8 load_op8(const float* p) {
 // (y0, y1] is covered by the first range; any ancestor of such a segment whose
 // run starts at or before y0 is an ancestor-or-self of s.  The ranges are
 // walked from s up to the root, tiles in descending order, and a tile already
-// visited through a later range is not visited again.
+// visited through a later range is not visited again.  All state is
+// wave-uniform (scalar registers).
 // ---------------------------------------------------------------------------
 template <int BN>
 struct TileCursor {
@@ -155,78 +192,68 @@ struct TileCursor {
     int seg;         // segment whose run is the current range (tree); -1 = done
     int own;         // current range is the query tile's own range
     int full_ok;     // every key of the current range is visible to every query row
-    int end_s;       // subtree end of the current segment (tree)
 
-    __device__ __forceinline__ static int64_t ceil_div(int64_t a, int64_t b) {
-        return a >= 0 ? (a + b - 1) / b : -((-a) / b);
-    }
-    __device__ __forceinline__ static int64_t floor_div(int64_t a, int64_t b) {
-        return a >= 0 ? a / b : -((-a + b - 1) / b);
-    }
+    __device__ __forceinline__ static int ceil_div(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
+    __device__ __forceinline__ static int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
-    // Key index range of the positions [pa, pb] inside the block; returns
-    // false if empty.
-    __device__ __forceinline__ bool set_range(int64_t pa, int64_t pb, const JobArgs& J) {
-        int64_t lo = ceil_div(pa - J.kbase, J.kstride);
-        int64_t hi = floor_div(pb - J.kbase, J.kstride);
-        if (lo < 0) lo = 0;
-        if (hi > J.n_k - 1) hi = J.n_k - 1;
+    // Key index range of the positions [pa, pb] inside the block; false if empty.
+    __device__ __forceinline__ bool set_range(int pa, int pb, const JobArgs& J) {
+        int lo, hi;
+        if (J.kstride == 1) {
+            lo = pa - J.kbase;
+            hi = pb - J.kbase;
+        } else {
+            lo = ceil_div(pa - J.kbase, J.kstride);
+            hi = floor_div(pb - J.kbase, J.kstride);
+        }
+        lo = max(lo, 0);
+        hi = min(hi, J.n_k - 1);
         if (lo > hi) return false;
-        j_lo = (int)lo;
-        j_hi = (int)hi;
-        int tl = j_lo / BN, th = j_hi / BN;
-        if (th >= visited_lo) th = visited_lo - 1;
-        t_lo = tl;
-        t = th;
+        j_lo = lo;
+        j_hi = hi;
+        t_lo = lo / BN;
+        t = min(hi / BN, visited_lo - 1);
         return true;
     }
 
-    __device__ void init(const JobArgs& J, const MaskArgs& M, int64_t y0, int64_t y1) {
+    __device__ void init(const JobArgs& J, const MaskArgs& M, int y0, int y1) {
         visited_lo = 0x7fffffff;
         own = 1;
         t = -1;
         t_lo = 0;
         if (M.kind == kCausal) {
             seg = -1;
-            end_s = 0x7fffffff;
             full_ok = 1;
             set_range(0, y1, J);
             return;
         }
         seg = wave_uniform(M.seg[y0]);
         int4 st = M.segtab[seg];
-        end_s = wave_uniform(st.w);
-        full_ok = (int64_t)end_s > y1;
-        if (!set_range(wave_uniform(st.x), y1, J)) t = t_lo - 1;
+        full_ok = wave_uniform(st.w) > y1;
+        if (!set_range(wave_uniform(st.x), y1, J)) t = -1;
     }
 
     // Produces the next tile; returns false when the walk is over.
-    __device__ bool next(const JobArgs& J, const MaskArgs& M, int64_t y0, int64_t y1,
-                         int* tile, int* full) {
+    __device__ bool next(const JobArgs& J, const MaskArgs& M, int y0, int y1, int* tile, int* full) {
         while (t < t_lo || t < 0) {
             // current range exhausted: move to the parent segment's run
             if (seg < 0) return false;
-            int4 st = M.segtab[seg];
-            int p = wave_uniform(st.z);
-            if (p < 0) { seg = -1; return false; }
+            int p = wave_uniform(M.segtab[seg].z);
             seg = p;
+            if (p < 0) return false;
             int4 sp = M.segtab[p];
             own = 0;
-            end_s = wave_uniform(sp.w);
-            full_ok = (int64_t)end_s > y1;
-            if (!set_range(wave_uniform(sp.x), (int64_t)wave_uniform(sp.y) - 1, J)) t = -1;
+            full_ok = wave_uniform(sp.w) > y1;
+            if (!set_range(wave_uniform(sp.x), wave_uniform(sp.y) - 1, J)) t = -1;
         }
-        int tt = t;
+        const int tt = t;
         --t;
-        if (tt < visited_lo) visited_lo = tt;
-        // classification: full iff the whole tile lies in the range, the tile is
-        // not ragged, every key precedes every query and all horizons pass y1.
-        int k0 = tt * BN, k1 = tt * BN + BN - 1;
-        int f = full_ok && k0 >= j_lo && k1 <= j_hi && k1 < J.n_k;
-        if (f && own) {
-            int64_t kmax = J.kbase + J.kstride * (int64_t)k1;
-            f = kmax <= y0;
-        }
+        visited_lo = tt;
+        // full iff the tile lies inside the range, is not ragged, every key
+        // precedes every query and every horizon passes y1
+        const int k0 = tt * BN, k1 = tt * BN + BN - 1;
+        int f = full_ok && k0 >= j_lo && k1 <= j_hi;
+        if (f && own) f = J.kbase + J.kstride * k1 <= y0;
         *tile = tt;
         *full = f;
         return true;
@@ -237,7 +264,7 @@ struct TileCursor {
 // the kernel
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BN>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 partial_attention_kernel(const LaunchArgs args) {
     using E = Elem<T>;
     using TL = Tile<T, D, BN>;
@@ -248,8 +275,7 @@ partial_attention_kernel(const LaunchArgs args) {
     // Workgroups are dispatched round-robin over the 8 XCDs; give every XCD a
     // contiguous range of work items so that the workgroups sharing one head's
     // K/V run on the same XCD and share its L2.
-    const int nwg = gridDim.x;
-    const int per_xcd = nwg / 8;
+    const int per_xcd = gridDim.x / 8;
     const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (w >= args.total_wg) return;
     int ji = 0;
@@ -259,31 +285,41 @@ partial_attention_kernel(const LaunchArgs args) {
     const int head = local / J.q_tiles;
     const int qtile = J.q_tiles - 1 - (local % J.q_tiles);   // heavy (late) tiles first
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int r32 = lane & 31;
     const int g = lane >> 5;
 
     const int q_first = qtile * kBM;
     const int q_last = min(q_first + kBM, J.n_q) - 1;
-    const int64_t y0 = J.qbase + J.qstride * (int64_t)q_first;
-    const int64_t y1 = J.qbase + J.qstride * (int64_t)q_last;
+    const int y0 = J.qbase + J.qstride * q_first;
+    const int y1 = J.qbase + J.qstride * q_last;
 
     // this lane's query row
     const int qi = q_first + wave * 32 + r32;
-    const bool q_valid = qi < J.n_q;
-    const int qi_ld = q_valid ? qi : J.n_q - 1;
-    const int64_t ypos = J.qbase + J.qstride * (int64_t)qi;
+    const int ypos = J.qbase + J.qstride * qi;
 
-    const T* qp = reinterpret_cast<const T*>(J.q) + head * J.q_sh + (int64_t)qi_ld * J.q_st;
-    const T* kp = reinterpret_cast<const T*>(J.k) + head * J.k_sh;
-    const T* vp = reinterpret_cast<const T*>(J.v) + head * J.v_sh;
+    const T* qh = reinterpret_cast<const T*>(J.q) + head * J.q_sh;
+    const T* kh = reinterpret_cast<const T*>(J.k) + head * J.k_sh;
+    const T* vh = reinterpret_cast<const T*>(J.v) + head * J.v_sh;
+    const auto qr = make_rsrc(qh, ((J.n_q - 1) * J.q_st + D) * (int)sizeof(T));
+    const auto kr = make_rsrc(kh, ((J.n_k - 1) * J.k_st + D) * (int)sizeof(T));
+    const auto vr = make_rsrc(vh, ((J.n_k - 1) * J.v_st + D) * (int)sizeof(T));
 
-    // Q^T operand: 8 consecutive dims per lane per 16-dim step
+    // Q^T operand: 8 consecutive dims per lane per 16-dim step (rows past the
+    // block read as zero; they are never stored)
     op8 qreg[TL::DSTEPS];
+    {
+        const int qoff = qi * J.q_st * (int)sizeof(T);
 #pragma unroll
-    for (int s = 0; s < TL::DSTEPS; ++s)
-        qreg[s] = load_op8(qp + s * 16 + 8 * g);
+        for (int s = 0; s < TL::DSTEPS; ++s) {
+            const int off = qoff + (s * 16 + 8 * g) * (int)sizeof(T);
+            u32x4 lo = buf_load16(qr, off);
+            u32x4 hi = sizeof(T) == 4 ? buf_load16(qr, off + 16) : lo;
+            qreg[s] = as_op8<T>(lo, hi);
+        }
+    }
 
     // permuted K row fed by this lane (see the header comment)
     const int kperm_i = (r32 >> 3) * 4 + (r32 & 3);
@@ -292,10 +328,14 @@ partial_attention_kernel(const LaunchArgs args) {
     f32x16 acc[TL::DBLK];
 #pragma unroll
     for (int b = 0; b < TL::DBLK; ++b) acc[b] = f32x16{};
-    float m_run = -INFINITY;   // running max of scaled scores (log2 domain)
+    float m_run = -INFINITY;   // running (lazily raised) max of scaled scores, base 2
     float l_run = 0.f;         // this lane's half of the running denominator
 
     // ---- staging registers -------------------------------------------------
+    // K: thread chunk c -> row c / (D/EPC), column chunk c % (D/EPC).
+    // V: thread group gi -> keys 4*(gi % KG) .. +3, dims EPC*(gi / KG) .. ;
+    //    consecutive lanes take consecutive key groups so that the transposed
+    //    LDS writes of one instruction fill consecutive 8-byte slots of a row.
     u32x4 kreg[TL::K_PER_THREAD];
     u32x4 vreg[TL::V_PER_THREAD][4];
     int endreg = 0;
@@ -305,28 +345,25 @@ partial_attention_kernel(const LaunchArgs args) {
         const int j0 = tile * BN;
 #pragma unroll
         for (int i = 0; i < TL::K_PER_THREAD; ++i) {
-            int c = threadIdx.x + i * kThreads;
+            const int c = tid + i * kThreads;
             if (c < TL::K_CHUNKS) {
-                int row = c / (D / TL::EPC), col = c % (D / TL::EPC);
-                int j = min(j0 + row, J.n_k - 1);
-                kreg[i] = *reinterpret_cast<const u32x4*>(kp + (int64_t)j * J.k_st + col * TL::EPC);
+                const int row = c / (D / TL::EPC), col = c % (D / TL::EPC);
+                kreg[i] = buf_load16(kr, ((j0 + row) * J.k_st + col * TL::EPC) * (int)sizeof(T));
             }
         }
 #pragma unroll
         for (int i = 0; i < TL::V_PER_THREAD; ++i) {
-            int gi = threadIdx.x + i * kThreads;
+            const int gi = tid + i * kThreads;
             if (gi < TL::V_GROUPS) {
-                int kg = gi / (D / TL::EPC), dc = gi % (D / TL::EPC);
+                const int kg = gi % TL::KG, dc = gi / TL::KG;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    int j = min(j0 + 4 * kg + r, J.n_k - 1);
-                    vreg[i][r] = *reinterpret_cast<const u32x4*>(vp + (int64_t)j * J.v_st + dc * TL::EPC);
-                }
+                for (int r = 0; r < 4; ++r)
+                    vreg[i][r] = buf_load16(vr, ((j0 + 4 * kg + r) * J.v_st + dc * TL::EPC) * (int)sizeof(T));
             }
         }
-        if (tree && threadIdx.x < BN) {
-            int j = j0 + threadIdx.x;
-            endreg = j < J.n_k ? args.mask.end[J.kbase + J.kstride * (int64_t)j] : (int)0x80000000;
+        if (tree && tid < BN) {
+            const int j = j0 + tid;
+            endreg = j < J.n_k ? args.mask.end[J.kbase + J.kstride * j] : (int)0x80000000;
         }
     };
 
@@ -336,39 +373,39 @@ partial_attention_kernel(const LaunchArgs args) {
         int* Es = reinterpret_cast<int*>(Vt + TL::V_ELEMS);
 #pragma unroll
         for (int i = 0; i < TL::K_PER_THREAD; ++i) {
-            int c = threadIdx.x + i * kThreads;
+            const int c = tid + i * kThreads;
             if (c < TL::K_CHUNKS) {
-                int row = c / (D / TL::EPC), col = c % (D / TL::EPC);
+                const int row = c / (D / TL::EPC), col = c % (D / TL::EPC);
                 *reinterpret_cast<u32x4*>(Ks + row * TL::KS + col * TL::EPC) = kreg[i];
             }
         }
 #pragma unroll
         for (int i = 0; i < TL::V_PER_THREAD; ++i) {
-            int gi = threadIdx.x + i * kThreads;
+            const int gi = tid + i * kThreads;
             if (gi < TL::V_GROUPS) {
-                int kg = gi / (D / TL::EPC), dc = gi % (D / TL::EPC);
+                const int kg = gi % TL::KG, dc = gi / TL::KG;
                 if constexpr (sizeof(T) == 2) {
-                    // 4 keys x 8 dims -> 8 dims x 4 keys; each output is 4 bf16
-                    // of one dim: pick 16-bit halves with v_perm_b32.
+                    // 4 keys x 8 dims -> 8 dims x 4 keys: each output is the 16-bit
+                    // half of one dim from each key (v_perm_b32 byte selects:
+                    // low half -> bytes 1:0, high half -> bytes 3:2)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int w32 = e >> 1;
-                        // byte selectors: low half -> bytes 1:0, high half -> bytes 3:2
                         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                        uint32_t lo = __builtin_amdgcn_perm(vreg[i][1][w32], vreg[i][0][w32], sel);
-                        uint32_t hi = __builtin_amdgcn_perm(vreg[i][3][w32], vreg[i][2][w32], sel);
+                        const uint32_t lo = __builtin_amdgcn_perm(vreg[i][1][w32], vreg[i][0][w32], sel);
+                        const uint32_t hi = __builtin_amdgcn_perm(vreg[i][3][w32], vreg[i][2][w32], sel);
                         *reinterpret_cast<u32x2*>(Vt + (dc * 8 + e) * TL::VS + 4 * kg) = u32x2{lo, hi};
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        u32x4 col = {vreg[i][0][e], vreg[i][1][e], vreg[i][2][e], vreg[i][3][e]};
+                        const u32x4 col = {vreg[i][0][e], vreg[i][1][e], vreg[i][2][e], vreg[i][3][e]};
                         *reinterpret_cast<u32x4*>(Vt + (dc * 4 + e) * TL::VS + 4 * kg) = col;
                     }
                 }
             }
         }
-        if (tree && threadIdx.x < BN) Es[threadIdx.x] = endreg;
+        if (tree && tid < BN) Es[tid] = endreg;
     };
 
     // ---- tile walk ------------------------------------------------------------
@@ -398,13 +435,11 @@ partial_attention_kernel(const LaunchArgs args) {
             s[kb] = f32x16{};
             const T* krow = Ks + (kb * 32 + kperm) * TL::KS + 8 * g;
 #pragma unroll
-            for (int ds = 0; ds < TL::DSTEPS; ++ds) {
-                op8 a = load_op8(krow + ds * 16);
-                s[kb] = E::mfma_k16(a, qreg[ds], s[kb]);
-            }
+            for (int ds = 0; ds < TL::DSTEPS; ++ds) s[kb] = E::mfma_k16(load_op8(krow + ds * 16), qreg[ds], s[kb]);
         }
 
-        // elementwise visibility on partial tiles: x <= y < end[x], key in range
+        // elementwise visibility on partial tiles: key in the block and
+        // kpos <= ypos < end[kpos]
         if (!full) {
 #pragma unroll
             for (int kb = 0; kb < TL::KB; ++kb) {
@@ -412,48 +447,50 @@ partial_attention_kernel(const LaunchArgs args) {
                 for (int i = 0; i < 16; ++i) {
                     const int jl = kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
                     const int j = tile * BN + jl;
-                    const int64_t x = J.kbase + J.kstride * (int64_t)j;
-                    bool vis = j < J.n_k && x <= ypos;
-                    if (tree) vis = vis && ypos < (int64_t)Es[jl];
+                    bool vis = j < J.n_k && J.kbase + J.kstride * j <= ypos;
+                    if (tree) vis = vis && ypos < Es[jl];
                     if (!vis) s[kb][i] = -INFINITY;
                 }
             }
         }
 
-        // online softmax for this lane's query
+        // online softmax for this lane's query, with a lazily raised max
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < TL::KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * c2);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        mx = xhalf_max(mx) * c2;
+        const bool raise = mx > m_run + kTau;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            // lanes that keep their max multiply by exactly 1 (their max may
+            // still be -inf, and -inf - -inf would be NaN)
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;   // 0 when m_run = -inf
+            l_run *= alpha;
+#pragma unroll
+            for (int b = 0; b < TL::DBLK; ++b) acc[b] *= alpha;
+            m_run = raise ? mx : m_run;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float psum = 0.f;
         op8 pb[TL::KSTEPS];
 #pragma unroll
         for (int kb = 0; kb < TL::KB; ++kb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m_use));
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m_use));
                 psum += p;
                 pb[kb * 2 + (i >> 3)][i & 7] = (T)p;
             }
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int b = 0; b < TL::DBLK; ++b) acc[b] *= alpha;
+        l_run += psum;
 
         // O^T += V^T P^T
 #pragma unroll
         for (int ks = 0; ks < TL::KSTEPS; ++ks) {
 #pragma unroll
-            for (int b = 0; b < TL::DBLK; ++b) {
-                op8 a = load_op8(Vt + (b * 32 + r32) * TL::VS + ks * 16 + 8 * g);
-                acc[b] = E::mfma_k16(a, pb[ks], acc[b]);
-            }
+            for (int b = 0; b < TL::DBLK; ++b)
+                acc[b] = E::mfma_k16(load_op8(Vt + (b * 32 + r32) * TL::VS + ks * 16 + 8 * g), pb[ks], acc[b]);
         }
 
         have = nhave;
@@ -463,11 +500,11 @@ partial_attention_kernel(const LaunchArgs args) {
     }
 
     // ---- epilogue: normalise, then write or merge ------------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = xhalf_sum(l_run);
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse_new = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-    if (!q_valid) return;
+    if (qi >= J.n_q) return;
     float* orow = J.o + (int64_t)head * J.n_q * D + (int64_t)qi * D;
     float* lrow = J.lse + (int64_t)head * J.n_q + qi;
     if (!J.accumulate) {
@@ -475,8 +512,8 @@ partial_attention_kernel(const LaunchArgs args) {
         for (int b = 0; b < TL::DBLK; ++b)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                f32x4 v = {acc[b][q4 * 4 + 0] * inv, acc[b][q4 * 4 + 1] * inv,
-                           acc[b][q4 * 4 + 2] * inv, acc[b][q4 * 4 + 3] * inv};
+                const f32x4 v = {acc[b][q4 * 4 + 0] * inv, acc[b][q4 * 4 + 1] * inv, acc[b][q4 * 4 + 2] * inv,
+                                 acc[b][q4 * 4 + 3] * inv};
                 *reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4) = v;
             }
         if (g == 0) *lrow = lse_new;
@@ -493,7 +530,7 @@ partial_attention_kernel(const LaunchArgs args) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 f32x4* dst = reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4);
-                f32x4 old = *dst;
+                const f32x4 old = *dst;
                 f32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = (wa * old[e] + wbn * acc[b][q4 * 4 + e]) * rz;
