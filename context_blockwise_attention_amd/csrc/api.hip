@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "../../include/cpattn.h"
+#include "attn_bf16_kernel.hpp"
 #include "attn_kernel.hpp"
 #include "merge_kernel.hpp"
 
@@ -269,11 +270,28 @@ static int launch_partial_t(LaunchArgs& a, hipStream_t st) {
     return CPATTN_OK;
 }
 
+template <int D>
+static int launch_bf16(LaunchArgs& a, hipStream_t st) {
+    const int smem = BfTile<D>::LDS_BYTES;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        attr_set = true;
+    }
+    const int grid = (a.total_wg + 7) / 8 * 8;
+    hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(grid), dim3(kThreads), smem, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "partial attention launch");
+    return CPATTN_OK;
+}
+
 static int launch_partial(LaunchArgs& a, int dtype, int d, hipStream_t st) {
     if (a.total_wg == 0) return CPATTN_OK;
     if (dtype == CPATTN_BF16) {
-        if (d == 128) return launch_partial_t<__bf16, 128, 64>(a, st);
-        return launch_partial_t<__bf16, 64, 64>(a, st);
+        if (d == 128) return launch_bf16<128>(a, st);
+        return launch_bf16<64>(a, st);
     }
     if (d == 128) return launch_partial_t<float, 128, 32>(a, st);
     return launch_partial_t<float, 64, 32>(a, st);

@@ -254,14 +254,66 @@ struct TileCursor {
         const int k0 = tt * BN, k1 = tt * BN + BN - 1;
         int f = full_ok && k0 >= j_lo && k1 <= j_hi;
         if (f && own) f = J.kbase + J.kstride * k1 <= y0;
-        *tile = tt;
-        *full = f;
+        *tile = wave_uniform(tt);
+        *full = wave_uniform(f);
         return true;
     }
 };
 
 // ---------------------------------------------------------------------------
-// the kernel
+// Epilogue shared by the kernels: lane (query qi, half g) holds the O^T
+// accumulators of its query (dims b*32 + (i/4)*8 + g*4 + i%4), the running
+// max m_run (base 2, scaled) and its half of the denominator.  Writes the
+// partial (O, LSE), or merges it into the running (O, LSE) already stored:
+// M = max(L_old, L_new), w = exp(L - M), O = (w_old O_old + w_new O_new) /
+// (w_old + w_new), L = M + log(w_old + w_new).  LSE is a natural log.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void write_result(const JobArgs& J, int head, int qi, int g, const f32x16* acc,
+                                             float m_run, float l_run) {
+    constexpr int DBLK = D / 32;
+    const float l_tot = xhalf_sum(l_run);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse_new = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    if (qi >= J.n_q) return;
+    float* orow = J.o + (int64_t)head * J.n_q * D + (int64_t)qi * D;
+    float* lrow = J.lse + (int64_t)head * J.n_q + qi;
+    if (!J.accumulate) {
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 v = {acc[b][q4 * 4 + 0] * inv, acc[b][q4 * 4 + 1] * inv, acc[b][q4 * 4 + 2] * inv,
+                                 acc[b][q4 * 4 + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4) = v;
+            }
+        if (g == 0) *lrow = lse_new;
+    } else {
+        const float lse_old = *lrow;
+        const float M = fmaxf(lse_old, lse_new);
+        if (M == -INFINITY) return;   // both sides empty: keep (0, -inf)
+        const float wa = expf(lse_old - M), wb = expf(lse_new - M);
+        const float z = wa + wb;
+        const float rz = 1.f / z;
+        const float wbn = wb * inv;
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4* dst = reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4);
+                const f32x4 old = *dst;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (wa * old[e] + wbn * acc[b][q4 * 4 + e]) * rz;
+                *dst = v;
+            }
+        if (g == 0) *lrow = M + logf(z);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the register-staged kernel (fp32 inputs; the bf16 path is attn_bf16_kernel.hpp)
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BN>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -282,12 +334,13 @@ partial_attention_kernel(const LaunchArgs args) {
     while (ji + 1 < args.n_jobs && w >= args.jobs[ji + 1].wg_begin) ++ji;
     const JobArgs& J = args.jobs[ji];
     const int local = w - J.wg_begin;
-    const int head = local / J.q_tiles;
-    const int qtile = J.q_tiles - 1 - (local % J.q_tiles);   // heavy (late) tiles first
+    // integer division runs on the vector ALU; keep the results scalar
+    const int head = wave_uniform(local / J.q_tiles);
+    const int qtile = wave_uniform(J.q_tiles - 1 - (local % J.q_tiles));   // heavy (late) tiles first
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = wave_uniform(tid >> 6);   // scalar: the wave index is uniform per wave
     const int r32 = lane & 31;
     const int g = lane >> 5;
 
@@ -500,44 +553,7 @@ partial_attention_kernel(const LaunchArgs args) {
     }
 
     // ---- epilogue: normalise, then write or merge ------------------------------
-    const float l_tot = xhalf_sum(l_run);
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse_new = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-    if (qi >= J.n_q) return;
-    float* orow = J.o + (int64_t)head * J.n_q * D + (int64_t)qi * D;
-    float* lrow = J.lse + (int64_t)head * J.n_q + qi;
-    if (!J.accumulate) {
-#pragma unroll
-        for (int b = 0; b < TL::DBLK; ++b)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 v = {acc[b][q4 * 4 + 0] * inv, acc[b][q4 * 4 + 1] * inv, acc[b][q4 * 4 + 2] * inv,
-                                 acc[b][q4 * 4 + 3] * inv};
-                *reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4) = v;
-            }
-        if (g == 0) *lrow = lse_new;
-    } else {
-        const float lse_old = *lrow;
-        const float M = fmaxf(lse_old, lse_new);
-        if (M == -INFINITY) return;   // both sides empty: keep (0, -inf)
-        const float wa = expf(lse_old - M), wb = expf(lse_new - M);
-        const float z = wa + wb;
-        const float rz = 1.f / z;
-        const float wbn = wb * inv;
-#pragma unroll
-        for (int b = 0; b < TL::DBLK; ++b)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                f32x4* dst = reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4);
-                const f32x4 old = *dst;
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (wa * old[e] + wbn * acc[b][q4 * 4 + e]) * rz;
-                *dst = v;
-            }
-        if (g == 0) *lrow = M + logf(z);
-    }
+    write_result<D>(J, head, qi, g, acc, m_run, l_run);
 }
 
 }  // namespace cpattn
