@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/cpattn.h declares, and rejects malformed or unsupported arguments
+with the documented status codes before any device work (no compute call is
+made here).  Pointers below are dummies that validation rejects first."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+OK, EINVAL, EUNSUPPORTED = 0, -1, -2
+
+
+@pytest.fixture(scope="module")
+def L():
+    from context_blockwise_attention_amd import build as b
+    if not b.up_to_date():
+        b.build()
+    import context_blockwise_attention_amd as cp
+    return cp.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpattn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = _declared()
+    assert "cpattn_partial" in names and "cpattn_ring_emulate" in names and "cpattn_merge" in names
+    for n in names:
+        assert hasattr(L, n), "libcpattn.so does not export %s" % n
+
+
+def test_version_and_error_string(L):
+    import context_blockwise_attention_amd as cp
+    assert cp.version() == (0, 1)
+    assert isinstance(L.cpattn_last_error(), bytes)
+
+
+def _tensor(cp, data=0x1000, dtype=0, H=2, n=16, d=128, sh=None, st=None):
+    st = d if st is None else st
+    sh = n * st if sh is None else sh
+    return cp._Tensor(data, dtype, 0, H, n, d, sh, st)
+
+
+def test_causal_mask_is_host_only(L):
+    h = ctypes.c_void_p()
+    assert L.cpattn_mask_causal(100, ctypes.byref(h)) == OK
+    assert L.cpattn_mask_npos(h) == 100
+    assert L.cpattn_mask_free(h) == OK
+    assert L.cpattn_mask_causal(-1, ctypes.byref(h)) == EINVAL
+    assert L.cpattn_mask_causal(5, None) == EINVAL
+
+
+@pytest.mark.parametrize("seg,parent,code", [
+    ([0, 0, 1, 1, 2, 2], [-1, -1, 0], EUNSUPPORTED),   # child stored outside its parent's subtree
+    ([0, 1, 0], [-1, 0], EINVAL),                      # segment 0 split into two runs
+    ([0, 0, 3], [-1, 0], EINVAL),                      # segment id out of range
+    ([0, 1], [1, 0], EINVAL),                          # parent cycle
+    ([0, 1], [-1, 5], EINVAL),                         # parent out of range
+    ([0, 0], [-1, 0], EINVAL),                         # segment 1 has no token
+    ([0, 0, 1, 1], [1, -1], EUNSUPPORTED),             # parent stored after its child
+])
+def test_tree_descriptor_rejections(L, seg, parent, code):
+    s = np.asarray(seg, dtype=np.int32)
+    p = np.asarray(parent, dtype=np.int32)
+    h = ctypes.c_void_p()
+    rc = L.cpattn_mask_tree(s.ctypes.data, len(s), p.ctypes.data, len(p), None, ctypes.byref(h))
+    assert rc == code, L.cpattn_last_error()
+    assert L.cpattn_last_error().startswith(b"cpattn_mask_tree")
+
+
+def _partial(L, cp, q, k, v, mask, qpos=(0, 1), kpos=(0, 1), scale=0.1, o=0x2000, lse=0x3000, acc=0):
+    return L.cpattn_partial(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), mask, cp._PosMap(*qpos),
+                            cp._PosMap(*kpos), scale, o, lse, acc, None)
+
+
+def test_partial_validation(L):
+    import context_blockwise_attention_amd as cp
+    h = ctypes.c_void_p()
+    assert L.cpattn_mask_causal(64, ctypes.byref(h)) == OK
+    t = _tensor(cp)
+    assert _partial(L, cp, _tensor(cp, dtype=7), t, t, h) == EUNSUPPORTED          # dtype
+    assert _partial(L, cp, _tensor(cp, d=96), t, t, h) == EUNSUPPORTED             # head dim
+    assert _partial(L, cp, t, _tensor(cp, dtype=1), t, h) == EUNSUPPORTED          # mixed dtypes
+    assert _partial(L, cp, t, _tensor(cp, H=3), t, h) == EINVAL                    # head counts differ
+    assert _partial(L, cp, t, t, _tensor(cp, n=15), h) == EINVAL                   # k/v lengths differ
+    assert _partial(L, cp, _tensor(cp, data=0x1008), t, t, h) == EUNSUPPORTED      # alignment
+    assert _partial(L, cp, _tensor(cp, st=132), t, t, h) == EUNSUPPORTED           # stride not x8
+    assert _partial(L, cp, t, t, t, None) == EINVAL                                # no mask
+    assert _partial(L, cp, t, t, t, h, scale=0.0) == EUNSUPPORTED                  # scale
+    assert _partial(L, cp, t, t, t, h, scale=float("nan")) == EUNSUPPORTED
+    assert _partial(L, cp, t, t, t, h, acc=2) == EINVAL                            # accumulate flag
+    assert _partial(L, cp, t, t, t, h, o=0) == EINVAL                              # no output
+    assert _partial(L, cp, t, t, t, h, o=0x2004) == EUNSUPPORTED                   # output alignment
+    assert _partial(L, cp, t, t, t, h, qpos=(60, 1)) == EINVAL                     # beyond the mask
+    assert _partial(L, cp, t, t, t, h, kpos=(0, 0)) == EINVAL                      # stride 0
+    assert _partial(L, cp, _tensor(cp, n=0), t, t, h) == OK                        # empty query block
+    huge = _tensor(cp, n=(1 << 23), st=256)
+    assert _partial(L, cp, huge, huge, huge, h) == EUNSUPPORTED                    # > 2 GiB per head
+    assert L.cpattn_mask_free(h) == OK
+
+
+def test_merge_and_ring_validation(L):
+    import context_blockwise_attention_amd as cp
+    P = ctypes.c_void_p
+    parts = (P * 65)(*([0x1000] * 65))
+    assert L.cpattn_merge(0, parts, parts, 10, 128, 0x2000, 0x3000, None) == EINVAL
+    assert L.cpattn_merge(65, parts, parts, 10, 128, 0x2000, 0x3000, None) == EINVAL
+    assert L.cpattn_merge(2, parts, parts, 10, 0, 0x2000, 0x3000, None) == EINVAL
+    assert L.cpattn_merge(2, parts, parts, 0, 128, 0x2000, 0x3000, None) == OK     # no rows: no-op
+    h = ctypes.c_void_p()
+    assert L.cpattn_mask_causal(64, ctypes.byref(h)) == OK
+    N = 2
+    ts = (cp._Tensor * N)(*[_tensor(cp) for _ in range(N)])
+    pos = (cp._PosMap * N)(cp._PosMap(0, 1), cp._PosMap(16, 1))
+    outs = (P * N)(0x2000, 0x2000)
+    assert L.cpattn_ring_emulate(0, ts, ts, ts, pos, None, 0, h, 0.1, outs, outs, None) == EINVAL
+    assert L.cpattn_ring_emulate(65, ts, ts, ts, pos, None, 65, h, 0.1, outs, outs, None) == EINVAL
+    bad = (ctypes.c_int * 1)(5)
+    assert L.cpattn_ring_emulate(N, ts, ts, ts, pos, bad, 1, h, 0.1, outs, outs, None) == EINVAL
+    dup = (ctypes.c_int * 2)(1, 1)
+    assert L.cpattn_ring_emulate(N, ts, ts, ts, pos, dup, 2, h, 0.1, outs, outs, None) == EINVAL
+    assert L.cpattn_ring_emulate(N, ts, ts, ts, pos, None, 1, h, 0.1, outs, outs, None) == EINVAL
+    far = (cp._PosMap * N)(cp._PosMap(0, 1), cp._PosMap(60, 1))
+    assert L.cpattn_ring_emulate(N, ts, ts, ts, far, None, N, h, 0.1, outs, outs, None) == EINVAL
+    assert L.cpattn_mask_free(h) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import context_blockwise_attention_amd as cp
+    monkeypatch.setattr(cp, "_lib", None)
+    monkeypatch.setattr(cp, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        cp.lib()

@@ -1,0 +1,281 @@
+"""GPU parity at the workloads' full sizes, through the C ABI, in the launch
+configuration the benchmark times (ring emulation of every rank):
+
+* sampled rows (256 per head) against the fp64 reference, which computes
+  plain unpartitioned attention on global positions -- the ring's merged
+  result must equal it (the merge is exact up to rounding);
+* every row against exact counts: with Q = 0 all visible keys get the same
+  weight, so with V[h, j, c] = bit (c % 17) of key j's position the output is
+  (visible keys with that bit) / (visible keys) and LSE = ln(visible keys),
+  computed here with integer arithmetic from the mask structure alone;
+* packed tree row against the five trajectories run separately;
+* two runs bitwise identical.
+
+Tolerances: bf16 inputs 2e-2 (O) / 1e-3 (LSE) max-abs; the count pin 1e-5.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_L = 2e-2, 1e-3
+BITS = 17
+
+
+@pytest.fixture(scope="module")
+def cp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_blockwise_attention_amd as cpattn
+    cpattn.lib()
+    return cpattn
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# exact visible-key counts (integer arithmetic on the mask structure)
+# ----------------------------------------------------------------------------
+def _bit_prefix(n):
+    """pref[b][x] = number of positions < x with bit b set."""
+    pos = np.arange(n, dtype=np.int64)
+    bits = ((pos[None, :] >> np.arange(BITS)[:, None]) & 1).astype(np.int64)
+    return np.concatenate([np.zeros((BITS, 1), np.int64), np.cumsum(bits, axis=1)], axis=1)
+
+
+def _expected_counts(n, q_pos, seg=None, parent=None):
+    """(counts[BITS, nq], n_vis[nq]) for queries at q_pos over keys at every
+    position < n, causal or tree."""
+    pref = _bit_prefix(n)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    if seg is None:
+        return pref[:, q_pos + 1], q_pos + 1
+    n_seg = len(parent)
+    starts = np.zeros(n_seg, np.int64)
+    ends = np.zeros(n_seg, np.int64)
+    for a, b in workloads.segment_bounds(seg):   # one contiguous run per segment
+        starts[seg[a]], ends[seg[a]] = a, b + 1
+    anc_cnt = np.zeros((n_seg, BITS), np.int64)
+    anc_len = np.zeros(n_seg, np.int64)
+    for s in range(n_seg):          # parents precede children in preorder
+        p = parent[s]
+        if p >= 0:
+            anc_cnt[s] = anc_cnt[p] + (pref[:, ends[p]] - pref[:, starts[p]])
+            anc_len[s] = anc_len[p] + (ends[p] - starts[p])
+    s_of = seg[q_pos]
+    counts = anc_cnt[s_of].T + pref[:, q_pos + 1] - pref[:, starts[s_of]]
+    n_vis = anc_len[s_of] + q_pos + 1 - starts[s_of]
+    return counts, n_vis
+
+
+def _bits_v(kpos, H, d):
+    kpos = np.asarray(kpos, dtype=np.int64)
+    c = np.arange(d) % BITS
+    v = ((kpos[:, None] >> c[None, :]) & 1).astype(np.float32)
+    return torch.from_numpy(np.broadcast_to(v, (H, len(kpos), d)).copy()).to(torch.bfloat16)
+
+
+def _check_counts(o, l, counts, n_vis, d, what):
+    c = np.arange(d) % BITS
+    exp_o = torch.from_numpy((counts[c, :] / n_vis[None, :]).T.astype(np.float32)).to(o.device)   # [nq, d]
+    exp_l = torch.from_numpy(np.log(n_vis.astype(np.float64)).astype(np.float32)).to(o.device)
+    do = float((o - exp_o[None]).abs().max())
+    dl = float((l - exp_l[None]).abs().max())
+    _print("  %s: count pin max|dO| %.2e max|dLSE| %.2e" % (what, do, dl))
+    assert do <= 1e-5 and dl <= 1e-5, what
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+def _sample(seed, H, n_q, forced):
+    return [workloads.sample_rows(seed, h, n_q, forced=forced) for h in range(H)]
+
+
+def _cmp_sampled(O_dev, L_dev, rows_by_head, q_cpu, k_cpu, v_cpu, q_pos, k_pos, omask, what):
+    """O_dev/L_dev: [H, n_q, d] / [H, n_q] device results for queries at
+    q_pos; compares rows_by_head[h] of each head with the reference."""
+    H = q_cpu.shape[0]
+    worst_o = worst_l = 0.0
+    for h in range(H):
+        rows = rows_by_head[h]
+        Oref, Lref = oracle.attention(q_cpu[h:h + 1], k_cpu[h:h + 1], v_cpu[h:h + 1], q_pos, k_pos, omask,
+                                      rows=rows)
+        idx = torch.from_numpy(rows).to(O_dev.device)
+        og = O_dev[h].index_select(0, idx).double().cpu().numpy()
+        lg = L_dev[h].index_select(0, idx).double().cpu().numpy()
+        worst_o = max(worst_o, float(np.abs(og - Oref[0]).max()))
+        worst_l = max(worst_l, float(np.abs(lg - Lref[0]).max()))
+    _print("  %s: sampled rows max|dO| %.2e max|dLSE| %.2e" % (what, worst_o, worst_l))
+    assert worst_o <= TOL_O and worst_l <= TOL_L, what
+
+
+def _contiguous_ring(cp, q, k, v, N, mask, ranks=None):
+    n = k.shape[1]
+    c = n // N
+    Q = [q[:, r * c:(r + 1) * c] for r in range(N)]
+    K = [k[:, r * c:(r + 1) * c] for r in range(N)]
+    V = [v[:, r * c:(r + 1) * c] for r in range(N)]
+    return cp.ring_emulate(Q, K, V, [(r * c, 1) for r in range(N)], mask, ranks=ranks)
+
+
+def _gather_rank_outputs(out, N, c, H, d):
+    O = torch.empty((H, N * c, d), dtype=torch.float32, device="cuda")
+    L = torch.empty((H, N * c), dtype=torch.float32, device="cuda")
+    for r, (o, l) in out.items():
+        O[:, r * c:(r + 1) * c] = o
+        L[:, r * c:(r + 1) * c] = l
+    return O, L
+
+
+# ----------------------------------------------------------------------------
+# causal ring: 32 heads, d 128, 32768 tokens, 8 blocks of 4096, all ranks
+# ----------------------------------------------------------------------------
+def test_causal_ring_8x4096(cp):
+    w = workloads.WORKLOADS["causal_ring"]
+    H, n, d, N = w.heads, w.n_tok, w.d, w.n_blocks
+    _print("causal_ring: generating inputs")
+    q, k, v = workloads.qkv(0, H, n, d, "bf16")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    mask = cp.Mask.causal(n)
+    out = _contiguous_ring(cp, qd, kd, vd, N, mask)
+    O, L = _gather_rank_outputs(out, N, n // N, H, d)
+    torch.cuda.synchronize()
+    forced = [0, n - 1] + [b * (n // N) for b in range(N)] + [b * (n // N) - 1 for b in range(1, N)]
+    pos = np.arange(n)
+    _cmp_sampled(O, L, _sample(0, H, n, forced), q, k, v, pos, pos, oracle.Causal(), "causal_ring")
+    # exact count pin on every row
+    vb = _bits_v(pos, H, d).cuda()
+    out = _contiguous_ring(cp, torch.zeros_like(qd), kd, vb, N, mask)
+    O, L = _gather_rank_outputs(out, N, n // N, H, d)
+    counts, n_vis = _expected_counts(n, pos)
+    _check_counts(O, L, counts, n_vis, d, "causal_ring")
+
+
+# ----------------------------------------------------------------------------
+# striped: P = 4 over 65536 positions, rank 0's 16384 queries
+# ----------------------------------------------------------------------------
+def test_striped_rank0(cp):
+    w = workloads.WORKLOADS["striped"]
+    H, n, d, P = w.heads, w.n_tok, w.d, w.n_blocks
+    _print("striped: generating inputs")
+    q, k, v = workloads.qkv(0, H, n, d, "bf16")   # row x of q/k/v = position x
+    lay = workloads.striped(n, P)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    Q = [qd[:, torch.from_numpy(p).cuda()].contiguous() for p in lay]
+    K = [kd[:, torch.from_numpy(p).cuda()].contiguous() for p in lay]
+    V = [vd[:, torch.from_numpy(p).cuda()].contiguous() for p in lay]
+    mask = cp.Mask.causal(n)
+    out = cp.ring_emulate(Q, K, V, [(r, P) for r in range(P)], mask, ranks=[0])
+    O, L = out[0]
+    torch.cuda.synchronize()
+    nq = n // P
+    forced = [0, nq - 1, 1, nq - 2]
+    pos = np.arange(n)
+    _cmp_sampled(O, L, _sample(0, H, nq, forced), q[:, lay[0]], k, v, lay[0], pos, oracle.Causal(), "striped")
+    vb = _bits_v(pos, H, d)
+    Vb = [vb[:, torch.from_numpy(p)].contiguous().cuda() for p in lay]
+    out = cp.ring_emulate([torch.zeros_like(Q[0])] + Q[1:], K, Vb, [(r, P) for r in range(P)], mask, ranks=[0])
+    counts, n_vis = _expected_counts(n, lay[0])
+    _check_counts(out[0][0], out[0][1], counts, n_vis, d, "striped")
+
+
+# ----------------------------------------------------------------------------
+# 64K tree row: prompt 24576 + 5 x 8192, N = 4 (timed), 1 and 8
+# ----------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tree64k(cp):
+    w = workloads.WORKLOADS["tree64k"]
+    H, n, d = w.heads, w.n_tok, w.d
+    _print("tree64k: generating inputs")
+    seg, parent = workloads.tree_prompt_completions(24576, (8192,) * 5)
+    q, k, v = workloads.qkv(0, H, n, d, "bf16")
+    return dict(H=H, n=n, d=d, seg=seg, parent=parent, q=q, k=k, v=v, qd=q.cuda(), kd=k.cuda(), vd=v.cuda(),
+                mask=cp.Mask.tree(seg, parent))
+
+
+@pytest.mark.parametrize("N", [4, 1, 8])
+def test_tree64k_ring(cp, tree64k, N):
+    t = tree64k
+    H, n, d = t["H"], t["n"], t["d"]
+    out = _contiguous_ring(cp, t["qd"], t["kd"], t["vd"], N, t["mask"])
+    O, L = _gather_rank_outputs(out, N, n // N, H, d)
+    torch.cuda.synchronize()
+    bounds = [b for ab in workloads.segment_bounds(t["seg"]) for b in ab]
+    forced = bounds + [r * (n // N) for r in range(N)]
+    pos = np.arange(n)
+    _cmp_sampled(O, L, _sample(1 + N, H, n, forced), t["q"], t["k"], t["v"], pos, pos,
+                 oracle.Tree(t["seg"], t["parent"]), "tree64k N=%d" % N)
+
+
+def test_tree64k_count_pin(cp, tree64k):
+    t = tree64k
+    H, n, d = t["H"], t["n"], t["d"]
+    pos = np.arange(n)
+    vb = _bits_v(pos, H, d).cuda()
+    out = _contiguous_ring(cp, torch.zeros_like(t["qd"]), t["kd"], vb, 4, t["mask"])
+    O, L = _gather_rank_outputs(out, 4, n // 4, H, d)
+    counts, n_vis = _expected_counts(n, pos, t["seg"], t["parent"])
+    _check_counts(O, L, counts, n_vis, d, "tree64k")
+
+
+def test_tree64k_packed_equals_separate(cp, tree64k):
+    """The packed row's outputs equal each 32768-token trajectory run alone as
+    a causal sequence (both on the GPU)."""
+    t = tree64k
+    H, n, d = t["H"], t["n"], t["d"]
+    out = _contiguous_ring(cp, t["qd"], t["kd"], t["vd"], 4, t["mask"])
+    O, L = _gather_rank_outputs(out, 4, n // 4, H, d)
+    P = 24576
+    causal = cp.Mask.causal(P + 8192)
+    worst_o = worst_l = 0.0
+    for c in range(5):
+        traj = torch.cat([torch.arange(P), torch.arange(P + 8192 * c, P + 8192 * (c + 1))]).cuda()
+        qs, ks, vs = (x.index_select(1, traj).contiguous() for x in (t["qd"], t["kd"], t["vd"]))
+        o, l = cp.partial(qs, ks, vs, causal)
+        worst_o = max(worst_o, float((o - O.index_select(1, traj)).abs().max()))
+        worst_l = max(worst_l, float((l - L.index_select(1, traj)).abs().max()))
+    _print("  packed vs separate: max|dO| %.2e max|dLSE| %.2e" % (worst_o, worst_l))
+    assert worst_o <= TOL_O and worst_l <= TOL_L
+
+
+def test_tree64k_deterministic(cp, tree64k):
+    t = tree64k
+    H, n, d = t["H"], t["n"], t["d"]
+    a = _gather_rank_outputs(_contiguous_ring(cp, t["qd"], t["kd"], t["vd"], 4, t["mask"]), 4, n // 4, H, d)
+    b = _gather_rank_outputs(_contiguous_ring(cp, t["qd"], t["kd"], t["vd"], 4, t["mask"]), 4, n // 4, H, d)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------
+# 131072-token row of seeded families, one GPU's share of a 4-way split
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tree128k_share(cp, seed):
+    w = workloads.WORKLOADS["tree128k_share"]
+    H, n, d, N = w.heads, w.n_tok, w.d, w.n_blocks
+    _print("tree128k seed %d: generating inputs" % seed)
+    seg, parent = workloads.tree_families(seed, n)
+    q, k, v = workloads.qkv(seed, H, n, d, "bf16")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    mask = cp.Mask.tree(seg, parent)
+    out = _contiguous_ring(cp, qd, kd, vd, N, mask)
+    O, L = _gather_rank_outputs(out, N, n // N, H, d)
+    torch.cuda.synchronize()
+    bounds = [b for ab in workloads.segment_bounds(seg) for b in ab]
+    pos = np.arange(n)
+    _cmp_sampled(O, L, _sample(seed, H, n, bounds), q, k, v, pos, pos, oracle.Tree(seg, parent),
+                 "tree128k seed %d" % seed)
+    vb = _bits_v(pos, H, d).cuda()
+    out = _contiguous_ring(cp, torch.zeros_like(qd), kd, vb, N, mask)
+    O, L = _gather_rank_outputs(out, N, n // N, H, d)
+    counts, n_vis = _expected_counts(n, pos, seg, parent)
+    _check_counts(O, L, counts, n_vis, d, "tree128k seed %d" % seed)
