@@ -35,6 +35,49 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bf16_kernel_tree64k.json")
+KERNEL_NAME = "attn_bf16_kernel<128>"
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; a traffic record is only used while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "context_blockwise_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_per_dispatch(csv_path, name_part, counter):
+    import csv
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals[int(r["Dispatch_Id"])] = vals.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals)]
+
+
+def traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, launches_per_step):
+    """HBM bytes per launch of the attention kernel from rocprofv3 FETCH_SIZE /
+    WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the same
+    counter read the known size of a plain device copy."""
+    f = _pmc_per_dispatch(fetch_csv, KERNEL_NAME, "FETCH_SIZE")
+    w = _pmc_per_dispatch(write_csv, KERNEL_NAME, "WRITE_SIZE")
+    cf = _pmc_per_dispatch(copy_fetch_csv, "", "FETCH_SIZE")
+    cw = _pmc_per_dispatch(copy_write_csv, "", "WRITE_SIZE")
+    copy_bytes = copy_mib * 2 ** 20
+    # the copy kernel is the largest dispatch of the calibration run
+    k_fetch = copy_bytes / (max(cf) * 1024.0)
+    k_write = copy_bytes / (max(cw) * 1024.0)
+    # one step = the last launches_per_step dispatches
+    f_step = sum(f[-launches_per_step:]) * 1024.0 * k_fetch
+    w_step = sum(w[-launches_per_step:]) * 1024.0 * k_write
+    return {"kernel": KERNEL_NAME, "source_hash": kernel_source_hash(),
+            "fetch_bytes_per_launch": f_step / launches_per_step,
+            "write_bytes_per_launch": w_step / launches_per_step,
+            "copy_factor_fetch": k_fetch, "copy_factor_write": k_write, "copy_mib": copy_mib}
 
 
 def tree_visible_pairs(seg: np.ndarray, parent: np.ndarray, q_rows: np.ndarray) -> np.ndarray:
@@ -62,7 +105,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample: query rows per head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing (diagnostic runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="calibration run: only time a plain device copy of this many MiB")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the traffic record from rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_record(*args.traffic_from, copy_mib=args.copy_mib or 1024, launches_per_step=args.blocks)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
               "(the ring's ranks are emulated on one GPU)" % args.gpus, file=sys.stderr)
@@ -73,6 +126,15 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
+    if args.copy_mib:
+        n = args.copy_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mib}))
+        return
     H, d = 32, 128
     P, C = 24576, (8192,) * 5
     seg, parent = workloads.tree_prompt_completions(P, C)
@@ -145,6 +207,11 @@ def main():
     merge_bytes = (N + 1) * H * c * (d + 1) * 4
     merge_gbs = merge_bytes / (merge_ms * 1e-3) / 1e9
 
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_hash") == kernel_source_hash() and rec.get("launches_per_step", launches) == launches:
+            traffic = round(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
     result = {
         "metric": "visible-pair attention TFLOP/s and % bf16 MFMA peak, 64K tree-packed row",
         "value": round(tflops, 2),
@@ -173,7 +240,7 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": "partial_attention_kernel<bf16,128,64>",
             "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "launches_per_step": launches, "avg_launch_ms": round(avg_launch_ms, 4),
             "visible_flops_per_launch": flops / launches,
         },
