@@ -35,8 +35,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bf16_kernel_tree64k.json")
-KERNEL_NAME = "attn_bf16_kernel<128>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bf16_pp_kernel_tree64k.json")
+KERNEL_NAME = "attn_bf16_pp_kernel<128>"
 
 
 def kernel_source_hash() -> str:
@@ -238,7 +238,7 @@ def main():
         "wall_ms_per_step": round(wall_ms / args.steps, 4),
         "descriptor_ms": {"first": round(desc_ms_first, 3), "median": round(float(np.median(desc_times)), 3)},
         "roofline": {
-            "bound": "mfma", "kernel": "partial_attention_kernel<bf16,128,64>",
+            "bound": "mfma", "kernel": KERNEL_NAME,
             "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "launches_per_step": launches, "avg_launch_ms": round(avg_launch_ms, 4),

@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = [os.path.join(PKG, "csrc", "api.hip")]
-DEPS = SRC + [os.path.join(PKG, "csrc", f) for f in ("attn_kernel.hpp", "merge_kernel.hpp")] + \
+DEPS = SRC + [os.path.join(PKG, "csrc", f) for f in os.listdir(os.path.join(PKG, "csrc")) if f.endswith(".hpp")] + \
     [os.path.join(ROOT, "include", "cpattn.h")]
 LIB = os.path.join(PKG, "libcpattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -272,16 +272,16 @@ static int launch_partial_t(LaunchArgs& a, hipStream_t st) {
 
 template <int D>
 static int launch_bf16(LaunchArgs& a, hipStream_t st) {
-    const int smem = BfTile<D>::LDS_BYTES;
+    const int smem = PPTile<D>::LDS_BYTES;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_pp_kernel<D>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
         attr_set = true;
     }
     const int grid = (a.total_wg + 7) / 8 * 8;
-    hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(grid), dim3(kThreads), smem, st, a);
+    hipLaunchKernelGGL((attn_bf16_pp_kernel<D>), dim3(grid), dim3(kPPThreads), smem, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "partial attention launch");
     return CPATTN_OK;
@@ -307,6 +307,9 @@ static MaskArgs mask_args(const cpattn_mask* m) {
     return ma;
 }
 
+// query rows per workgroup of the kernel that serves a dtype
+static int rows_per_wg(int dtype) { return dtype == CPATTN_BF16 ? kPPBM : kBM; }
+
 static JobArgs make_job(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, cpattn_posmap qp,
                         cpattn_posmap kp, float* o, float* lse, int accumulate) {
     JobArgs j{};
@@ -328,7 +331,8 @@ static JobArgs make_job(const cpattn_tensor* q, const cpattn_tensor* k, const cp
     j.n_q = (int32_t)q->n_tok;
     j.n_k = (int32_t)k->n_tok;
     j.accumulate = accumulate;
-    j.q_tiles = (int32_t)((q->n_tok + kBM - 1) / kBM);
+    const int bm = rows_per_wg(q->dtype);
+    j.q_tiles = (int32_t)((q->n_tok + bm - 1) / bm);
     return j;
 }
 

@@ -114,12 +114,13 @@ int cpattn_mask_free(cpattn_mask* m);
 /* Number of positions a descriptor covers (its n_pos / n_tok), or -1. */
 int64_t cpattn_mask_npos(const cpattn_mask* m);
 
-/* Partial attention of one query block against one key/value block.
+/* Partial attention of one query block against one key/value block: the
+ * (O, LSE) pair of one ring round ("Context Parallelism in ART", sections 02
+ * and 03; the masks are those of section 02).
  *   q: [H][n_q][d], k and v: [H][n_k][d]; one dtype, one d, one H.
  *   q_pos, k_pos: global positions of the rows (checked against the mask's
  *                 n_pos: every row's position must lie in [0, n_pos)).
  *   scale: multiplies q.k before the softmax (usually 1/sqrt(d)).
- *   o: fp32, element (h, i, c) at o[h*o_stride_head + i*d + c]... see below.
  *   o_out / lse_out: fp32 device arrays [H][n_q][d] and [H][n_q], contiguous.
  *   accumulate = 0: write the partial (O, LSE).
  *   accumulate = 1: read the running (O, LSE) already in o_out/lse_out and
