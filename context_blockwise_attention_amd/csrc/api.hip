@@ -345,16 +345,19 @@ static int run_jobs(std::vector<JobArgs>& jobs, const cpattn_mask* m, int heads,
         a.mask = mask_args(m);
         a.heads = heads;
         a.scale_log2 = scale_log2;
-        int64_t total = 0;
         int n = 0;
+        int64_t max_qt = 0;
         for (size_t i = first; i < jobs.size() && n < kMaxJobs; ++i, ++n) {
             a.jobs[n] = jobs[i];
-            a.jobs[n].wg_begin = (int32_t)total;
-            total += (int64_t)jobs[i].q_tiles * heads;
+            max_qt = std::max<int64_t>(max_qt, jobs[i].q_tiles);
         }
-        if (total > INT32_MAX / 2) return fail(CPATTN_EUNSUPPORTED, "too many workgroups in one launch");
+        // work slots: see work_item() in attn_kernel.hpp
+        a.heads_per_xcd = heads >= 8 ? (heads + 7) / 8 : 0;
+        const int64_t slots = a.heads_per_xcd > 0 ? 8 * (int64_t)a.heads_per_xcd * n * max_qt : (int64_t)heads * n * max_qt;
+        if (slots > INT32_MAX / 2) return fail(CPATTN_EUNSUPPORTED, "too many workgroups in one launch");
         a.n_jobs = n;
-        a.total_wg = (int32_t)total;
+        a.max_q_tiles = (int32_t)max_qt;
+        a.total_wg = (int32_t)slots;
         int rc = launch_partial(a, dtype, d, st);
         if (rc != CPATTN_OK) return rc;
     }

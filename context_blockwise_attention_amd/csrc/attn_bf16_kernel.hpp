@@ -30,6 +30,49 @@ __device__ __forceinline__ lds_byte* to_lds(void* p) { return (lds_byte*)(p); }
 __device__ __forceinline__ bf16x8 lds_op(const lds_byte* p) {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
 }
+// Raw buffer descriptor (base, stride 0, size in bytes, the flags of
+// make_rsrc) as four scalar registers, for the inline-asm loads below.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, int32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = wave_uniform((int32_t)(uint32_t)a);
+    r[1] = wave_uniform((int32_t)((a >> 32) & 0xffffu));
+    r[2] = wave_uniform(bytes);
+    r[3] = kBufferFlags;
+    return r;
+}
+// Direct global -> LDS loads (buffer_load ... lds): lane l's 16 (or 4) bytes
+// at buffer offset voff land at LDS byte address lds + 16 l (4 l); offsets
+// past the buffer's size read as zero.  They are issued as inline asm so that
+// the compiler does not make later LDS reads wait for them: the kernel tracks
+// them itself (vmcnt) and synchronises the workgroup before any wave reads
+// the destination.  Loads complete in issue order.  The LDS base travels in
+// m0, which the asm saves and restores (the compiler treats m0 as reserved);
+// GFX9 needs one wait state between an SALU write of m0 and the LDS-DMA
+// instruction that reads it, hence the s_nop.
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, int voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "memory");
+}
+__device__ __forceinline__ void dma_b32(i32x4 rsrc, int voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(lds)
+        : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const lds_byte* p) {
+    return (uint32_t)wave_uniform((int32_t)(uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+
 // transposed 4 x 16-bit read (see the header comment)
 __device__ __forceinline__ u32x2 lds_tr4(const lds_byte* p) {
     i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -48,10 +91,14 @@ __device__ __forceinline__ u32x2 lds_tr4(const lds_byte* p) {
 //
 // group 0 runs M(0) V(0) M(1) V(1) ..., group 1 the same one phase later, so
 // every SIMD always holds one wave in an MFMA phase and one in a softmax
-// phase.  Loads: at barrier 2t (t = tile sequence index) every wave issues
-// its share of K(t+1) and E(t+1) and of V(t); those land before barrier
-// 2t+2, which waits for them; buffers rotate K/V by 2 and E by 3, so a load
-// never overwrites data that a phase between its issue and its wait reads.
+// phase.  Loads run two iterations ahead: at barrier 2t (t = tile sequence
+// index) every wave issues its share of K(t+2), E(t+2) and V(t+1), and before
+// barrier 2t+2 it waits only for the loads it issued at barrier 2t-2, so a
+// tile's HBM/L2 latency is hidden behind two iterations of work (all
+// workgroups of a head walk the same tiles at about the same time, so most of
+// them wait on the same miss).  K and V rotate over 3 buffers, E over 4: a
+// load never overwrites data that a phase between its issue and its wait
+// reads.
 // ---------------------------------------------------------------------------
 constexpr int kPPThreads = 512;
 constexpr int kPPBM = 256;
@@ -68,9 +115,9 @@ struct PPTile {
     static constexpr int DBLK = D / 32;
     static constexpr int KSTEPS = BN / 16;
     static constexpr int K_OFF = 0;
-    static constexpr int V_OFF = 2 * TILE_BYTES;
-    static constexpr int E_OFF = 4 * TILE_BYTES;
-    static constexpr int LDS_BYTES = E_OFF + 3 * BN * 4;
+    static constexpr int V_OFF = 3 * TILE_BYTES;
+    static constexpr int E_OFF = 6 * TILE_BYTES;
+    static constexpr int LDS_BYTES = E_OFF + 4 * BN * 4;
 };
 
 template <int D>
@@ -82,15 +129,12 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     constexpr int ROWB = TT::ROWB;
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
-    const int per_xcd = gridDim.x / 8;
-    const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (w >= args.total_wg) return;
-    int ji = 0;
-    while (ji + 1 < args.n_jobs && w >= args.jobs[ji + 1].wg_begin) ++ji;
+    int ji, head, qtile;
+    if (!work_item(args, blockIdx.x, &ji, &head, &qtile)) return;
+    ji = wave_uniform(ji);
+    head = wave_uniform(head);
+    qtile = wave_uniform(qtile);
     const JobArgs& J = args.jobs[ji];
-    const int local = w - J.wg_begin;
-    const int head = wave_uniform(local / J.q_tiles);
-    const int qtile = wave_uniform(J.q_tiles - 1 - (local % J.q_tiles));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -138,20 +182,27 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             const int b = i * 8 + wave;
             const int row0 = j0 + b * TT::RPB;
             const int bytes = row0 < J.n_k ? (J.n_k - 1 - row0) * st * 2 + D * 2 : 0;
-            const auto r = make_rsrc(base + (int64_t)row0 * st, bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + b * 1024, 16, voff, 0, 0, 0);
+            dma_b128(sgpr_rsrc(base + (int64_t)row0 * st, bytes), voff, lds_addr(dst + b * 1024));
         }
     };
     auto issue_e = [&](int tile, lds_byte* dst) {
         if (wave == 0) {
             const int p0 = J.kbase + J.kstride * tile * BN;
-            const auto r = make_rsrc(args.mask.end + p0, (args.mask.n_pos - p0) * 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, lane * J.kstride * 4, 0, 0, 0);
+            dma_b32(sgpr_rsrc(args.mask.end + p0, (args.mask.n_pos - p0) * 4), lane * J.kstride * 4, lds_addr(dst));
         }
     };
-    auto kbuf = [&](int s) { return lds + TT::K_OFF + (s & 1) * TT::TILE_BYTES; };
-    auto vbuf = [&](int s) { return lds + TT::V_OFF + (s & 1) * TT::TILE_BYTES; };
-    auto ebuf = [&](int s) { return lds + TT::E_OFF + (s % 3) * BN * 4; };
+    auto kbuf = [&](int s) { return lds + TT::K_OFF + (s % 3) * TT::TILE_BYTES; };
+    auto vbuf = [&](int s) { return lds + TT::V_OFF + (s % 3) * TT::TILE_BYTES; };
+    auto ebuf = [&](int s) { return lds + TT::E_OFF + (s & 3) * BN * 4; };
+    // Wait until at most `pending` of this wave's vector-memory loads are in
+    // flight (vmcnt only; the immediate leaves expcnt and lgkmcnt unwaited).
+    // Loads complete in issue order, so this waits for every older load.
+    auto wait_older = [&](int pending) {
+        if (pending >= 2 * TT::NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * TT::NI + 1));
+        else if (pending >= 2 * TT::NI) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * TT::NI));
+        else if (pending >= TT::NI) __builtin_amdgcn_s_waitcnt(0xF70 | TT::NI);
+        else __builtin_amdgcn_s_waitcnt(0xF70);
+    };
 
     const int kperm_i = (r32 >> 3) * 4 + (r32 & 3);
     const int kperm = (kperm_i >> 3) * 16 + ((r32 & 7) >> 2) * 8 + (kperm_i & 7);
@@ -296,18 +347,28 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         if (group != G) continue;
         TileCursor<BN> cur;
         cur.init(J, args.mask, y0, y1);
-        int t_cur = 0, f_cur = 0, t_nxt = 0, f_nxt = 0;
+        // tiles t, t+1, t+2 of the walk (h_*: whether they exist)
+        int t_cur = 0, f_cur = 0, t_nxt = 0, f_nxt = 0, t_n2 = 0, f_n2 = 0;
         if (!cur.next(J, args.mask, y0, y1, &t_cur, &f_cur)) break;   // tile 0
+        bool h_nxt = cur.next(J, args.mask, y0, y1, &t_nxt, &f_nxt);
+        bool h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+        const int e_loads = (tree && wave == 0) ? 1 : 0;   // horizon loads per tile of this wave
+        // prologue: K(0), E(0), then K(1), E(1), V(0), which may stay in flight
         issue_kv(kh, J.k_st, voff_k, t_cur, kbuf(0));
         if (tree) issue_e(t_cur, ebuf(0));
-        bool h_nxt = cur.next(J, args.mask, y0, y1, &t_nxt, &f_nxt);
-        __builtin_amdgcn_s_waitcnt(0);
-        phase_barrier();                                                // barrier 0
         if (h_nxt) {
             issue_kv(kh, J.k_st, voff_k, t_nxt, kbuf(1));
             if (tree) issue_e(t_nxt, ebuf(1));
         }
         issue_kv(vh, J.v_st, voff_v, t_cur, vbuf(0));
+        wait_older((h_nxt ? TT::NI + e_loads : 0) + TT::NI);
+        phase_barrier();                                                // barrier 0
+        if (h_n2) {
+            issue_kv(kh, J.k_st, voff_k, t_n2, kbuf(2));
+            if (tree) issue_e(t_n2, ebuf(2));
+        }
+        if (h_nxt) issue_kv(vh, J.v_st, voff_v, t_nxt, vbuf(1));
+        int pending = (h_n2 ? TT::NI + e_loads : 0) + (h_nxt ? TT::NI : 0);
         if (G == 0) {
             qk(kbuf(0));
             m_schedule(false, true);
@@ -323,14 +384,18 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             const int t_prev = t_cur, f_prev = f_cur;
             t_cur = t_nxt;
             f_cur = f_nxt;
-            h_nxt = cur.next(J, args.mask, y0, y1, &t_nxt, &f_nxt);
-            __builtin_amdgcn_s_waitcnt(0);
+            t_nxt = t_n2;
+            f_nxt = f_n2;
+            h_nxt = h_n2;
+            h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+            wait_older(pending);                                        // K(t), E(t), V(t-1) landed
             phase_barrier();                                            // barrier 2t
-            if (h_nxt) {
-                issue_kv(kh, J.k_st, voff_k, t_nxt, kbuf(t + 1));
-                if (tree) issue_e(t_nxt, ebuf(t + 1));
+            if (h_n2) {
+                issue_kv(kh, J.k_st, voff_k, t_n2, kbuf(t + 2));
+                if (tree) issue_e(t_n2, ebuf(t + 2));
             }
-            issue_kv(vh, J.v_st, voff_v, t_cur, vbuf(t));
+            if (h_nxt) issue_kv(vh, J.v_st, voff_v, t_nxt, vbuf(t + 1));
+            pending = (h_n2 ? TT::NI + e_loads : 0) + (h_nxt ? TT::NI : 0);
             if (G == 0) {
                 pv(vbuf(t - 1));
                 qk(kbuf(t));
@@ -346,8 +411,9 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             }
             ++t;
         }
-        // last iteration t = T: only tile T-1 (= cur) remains
-        __builtin_amdgcn_s_waitcnt(0);
+        // last iteration t = T: only tile T-1 (= cur) remains; nothing is in flight
+        // but V(T-1) (pending is 0 after the iteration that had no next tile)
+        wait_older(pending);
         phase_barrier();                                                // barrier 2T
         if (G == 0) {
             pv(vbuf(t - 1));

@@ -62,8 +62,7 @@ struct JobArgs {
     int32_t kbase, kstride;        // same for key rows
     int32_t n_q, n_k;
     int32_t accumulate;
-    int32_t q_tiles;   // ceil(n_q / kBM)
-    int32_t wg_begin;  // first work item of this job
+    int32_t q_tiles;   // ceil(n_q / rows per workgroup)
 };
 
 struct MaskArgs {
@@ -79,9 +78,45 @@ struct LaunchArgs {
     MaskArgs mask;
     int32_t n_jobs;
     int32_t heads;
-    int32_t total_wg;   // work items (the grid is rounded up to a multiple of 8)
-    float scale_log2;   // scale * log2(e)
+    int32_t total_wg;        // work slots = grid size (some slots may be empty)
+    int32_t max_q_tiles;     // largest q_tiles among the jobs
+    int32_t heads_per_xcd;   // ceil(heads / 8) with at least 8 heads, else 0
+    float scale_log2;        // scale * log2(e)
 };
+
+// ---------------------------------------------------------------------------
+// Work slot of workgroup `bid` -> (job, head, q-tile), or false for an empty
+// slot.  Work items are ordered by q-tile rank counted from the heavy end
+// (rank 0 = a job's last q-tile, whose queries see the most keys), then job,
+// then head, so heavy items of every job start first.  Workgroups are
+// dispatched round-robin over the 8 XCDs (bid % 8).  With at least 8 heads,
+// XCD x runs, in that order, the items of the heads h with h % 8 == x: every
+// XCD gets the same share of every job (no XCD is left with only the light
+// job of a launch), and the q-tiles of one head, which read the same K/V, share
+// one L2.  With fewer heads the items go round-robin over the XCDs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool work_item(const LaunchArgs& a, int bid, int* job, int* head, int* qtile) {
+    int r, j, h;
+    if (a.heads_per_xcd > 0) {
+        const int x = bid & 7, p = bid >> 3;
+        const int per_rank = a.n_jobs * a.heads_per_xcd;
+        r = p / per_rank;
+        const int rem = p - r * per_rank;
+        j = rem / a.heads_per_xcd;
+        h = x + 8 * (rem - j * a.heads_per_xcd);
+    } else {
+        const int per_rank = a.n_jobs * a.heads;
+        r = bid / per_rank;
+        const int rem = bid - r * per_rank;
+        j = rem / a.heads;
+        h = rem - j * a.heads;
+    }
+    if (j >= a.n_jobs || h >= a.heads || r >= a.jobs[j].q_tiles) return false;
+    *job = j;
+    *head = h;
+    *qtile = a.jobs[j].q_tiles - 1 - r;
+    return true;
+}
 
 // ---------------------------------------------------------------------------
 // element traits
@@ -323,20 +358,14 @@ partial_attention_kernel(const LaunchArgs args) {
     using op8 = typename E::op8;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-    // ---- work item: XCD-aware mapping -----------------------------------
-    // Workgroups are dispatched round-robin over the 8 XCDs; give every XCD a
-    // contiguous range of work items so that the workgroups sharing one head's
-    // K/V run on the same XCD and share its L2.
-    const int per_xcd = gridDim.x / 8;
-    const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (w >= args.total_wg) return;
-    int ji = 0;
-    while (ji + 1 < args.n_jobs && w >= args.jobs[ji + 1].wg_begin) ++ji;
-    const JobArgs& J = args.jobs[ji];
-    const int local = w - J.wg_begin;
+    // ---- work item ------------------------------------------------------
+    int ji, head, qtile;
+    if (!work_item(args, blockIdx.x, &ji, &head, &qtile)) return;
     // integer division runs on the vector ALU; keep the results scalar
-    const int head = wave_uniform(local / J.q_tiles);
-    const int qtile = wave_uniform(J.q_tiles - 1 - (local % J.q_tiles));   // heavy (late) tiles first
+    ji = wave_uniform(ji);
+    head = wave_uniform(head);
+    qtile = wave_uniform(qtile);
+    const JobArgs& J = args.jobs[ji];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
