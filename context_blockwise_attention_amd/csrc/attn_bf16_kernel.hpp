@@ -134,7 +134,9 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     ji = wave_uniform(ji);
     head = wave_uniform(head);
     qtile = wave_uniform(qtile);
-    const JobArgs& J = args.jobs[ji];
+    // a copy, so that the fields the tile loop uses stay in scalar registers
+    // instead of being reloaded from the kernel arguments at every tile
+    const JobArgs J = args.jobs[ji];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -175,21 +177,27 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     const int rmod = (wave * TT::RPB + lrow) % CPR;
     const int voff_k = lrow * J.k_st * 2 + ((lslot ^ rmod) * 16);
     const int voff_v = lrow * J.v_st * 2 + ((lslot ^ ((4 * rmod) % CPR)) * 16);
-    auto issue_kv = [&](const __bf16* base, int st, int voff, int tile, lds_byte* dst) {
-        const int j0 = tile * BN;
+    // The head's K and V blocks (and the horizon array) as whole buffers: the
+    // ragged tail of the last tile lies past the buffer's size and reads as
+    // zero.  Per tile only the row offset (scalar) is added to each lane's
+    // constant offset; all offsets stay below 2 GiB (checked on the host).
+    const i32x4 k_rsrc = sgpr_rsrc(kh, (J.n_k - 1) * J.k_st * 2 + D * 2);
+    const i32x4 v_rsrc = sgpr_rsrc(vh, (J.n_k - 1) * J.v_st * 2 + D * 2);
+    const i32x4 e_rsrc = sgpr_rsrc(args.mask.end, args.mask.n_pos * 4);
+    int voffk[TT::NI], voffv[TT::NI];
 #pragma unroll
-        for (int i = 0; i < TT::NI; ++i) {
-            const int b = i * 8 + wave;
-            const int row0 = j0 + b * TT::RPB;
-            const int bytes = row0 < J.n_k ? (J.n_k - 1 - row0) * st * 2 + D * 2 : 0;
-            dma_b128(sgpr_rsrc(base + (int64_t)row0 * st, bytes), voff, lds_addr(dst + b * 1024));
-        }
+    for (int i = 0; i < TT::NI; ++i) {
+        const int rows = (i * 8 + wave) * TT::RPB;   // first row of this wave's i-th 1 KB block
+        voffk[i] = voff_k + rows * J.k_st * 2;
+        voffv[i] = voff_v + rows * J.v_st * 2;
+    }
+    auto issue_kv = [&](const i32x4& rsrc, const int* voffs, int st, int tile, lds_byte* dst) {
+        const int tile_bytes = tile * BN * st * 2;
+#pragma unroll
+        for (int i = 0; i < TT::NI; ++i) dma_b128(rsrc, voffs[i] + tile_bytes, lds_addr(dst + (i * 8 + wave) * 1024));
     };
     auto issue_e = [&](int tile, lds_byte* dst) {
-        if (wave == 0) {
-            const int p0 = J.kbase + J.kstride * tile * BN;
-            dma_b32(sgpr_rsrc(args.mask.end + p0, (args.mask.n_pos - p0) * 4), lane * J.kstride * 4, lds_addr(dst));
-        }
+        if (wave == 0) dma_b32(e_rsrc, (J.kbase + J.kstride * (tile * BN + lane)) * 4, lds_addr(dst));
     };
     auto kbuf = [&](int s) { return lds + TT::K_OFF + (s % 3) * TT::TILE_BYTES; };
     auto vbuf = [&](int s) { return lds + TT::V_OFF + (s % 3) * TT::TILE_BYTES; };
@@ -354,20 +362,20 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         bool h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
         const int e_loads = (tree && wave == 0) ? 1 : 0;   // horizon loads per tile of this wave
         // prologue: K(0), E(0), then K(1), E(1), V(0), which may stay in flight
-        issue_kv(kh, J.k_st, voff_k, t_cur, kbuf(0));
+        issue_kv(k_rsrc, voffk, J.k_st, t_cur, kbuf(0));
         if (tree) issue_e(t_cur, ebuf(0));
         if (h_nxt) {
-            issue_kv(kh, J.k_st, voff_k, t_nxt, kbuf(1));
+            issue_kv(k_rsrc, voffk, J.k_st, t_nxt, kbuf(1));
             if (tree) issue_e(t_nxt, ebuf(1));
         }
-        issue_kv(vh, J.v_st, voff_v, t_cur, vbuf(0));
+        issue_kv(v_rsrc, voffv, J.v_st, t_cur, vbuf(0));
         wait_older((h_nxt ? TT::NI + e_loads : 0) + TT::NI);
         phase_barrier();                                                // barrier 0
         if (h_n2) {
-            issue_kv(kh, J.k_st, voff_k, t_n2, kbuf(2));
+            issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(2));
             if (tree) issue_e(t_n2, ebuf(2));
         }
-        if (h_nxt) issue_kv(vh, J.v_st, voff_v, t_nxt, vbuf(1));
+        if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(1));
         int pending = (h_n2 ? TT::NI + e_loads : 0) + (h_nxt ? TT::NI : 0);
         if (G == 0) {
             qk(kbuf(0));
@@ -391,10 +399,10 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             wait_older(pending);                                        // K(t), E(t), V(t-1) landed
             phase_barrier();                                            // barrier 2t
             if (h_n2) {
-                issue_kv(kh, J.k_st, voff_k, t_n2, kbuf(t + 2));
+                issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(t + 2));
                 if (tree) issue_e(t_n2, ebuf(t + 2));
             }
-            if (h_nxt) issue_kv(vh, J.v_st, voff_v, t_nxt, vbuf(t + 1));
+            if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(t + 1));
             pending = (h_n2 ? TT::NI + e_loads : 0) + (h_nxt ? TT::NI : 0);
             if (G == 0) {
                 pv(vbuf(t - 1));
