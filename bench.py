@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bf16_pp_kernel_tree64k.json")
-KERNEL_NAME = "attn_bf16_pp_kernel<128>"
+KERNEL_NAME = "attn_bf16_pp_kernel<128, 64, 2>"
 
 
 def kernel_source_hash() -> str:

@@ -270,18 +270,25 @@ static int launch_partial_t(LaunchArgs& a, hipStream_t st) {
     return CPATTN_OK;
 }
 
+// bf16 partial attention: key-tile width and prefetch distance of the
+// ping-pong kernel (see attn_bf16_kernel.hpp)
+constexpr int kBf16BN = 64;
+constexpr int kBf16PF = 2;
+
 template <int D>
 static int launch_bf16(LaunchArgs& a, hipStream_t st) {
-    const int smem = PPTile<D>::LDS_BYTES;
+    using TT = PPTile<D, kBf16BN, kBf16PF>;
+    const auto kern = attn_bf16_pp_kernel<D, kBf16BN, kBf16PF>;
+    const int smem = TT::LDS_BYTES;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_pp_kernel<D>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
         attr_set = true;
     }
     const int grid = (a.total_wg + 7) / 8 * 8;
-    hipLaunchKernelGGL((attn_bf16_pp_kernel<D>), dim3(grid), dim3(kPPThreads), smem, st, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPPThreads), smem, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "partial attention launch");
     return CPATTN_OK;

@@ -98,14 +98,17 @@ __device__ __forceinline__ u32x2 lds_tr4(const lds_byte* p) {
 // workgroups of a head walk the same tiles at about the same time, so most of
 // them wait on the same miss).  K and V rotate over 3 buffers, E over 4: a
 // load never overwrites data that a phase between its issue and its wait
-// reads.
+// reads.  (Wider key tiles would halve the barriers per key, but 128-key
+// scores and probabilities do not fit the 256 registers a wave has at two
+// waves per SIMD.)
 // ---------------------------------------------------------------------------
 constexpr int kPPThreads = 512;
 constexpr int kPPBM = 256;
 
-template <int D>
+template <int D, int BN_, int PF_>
 struct PPTile {
-    static constexpr int BN = 64;
+    static constexpr int BN = BN_;                     // keys per tile
+    static constexpr int PF = PF_;                     // prefetch distance (iterations)
     static constexpr int CPR = D / 8;
     static constexpr int ROWB = D * 2;
     static constexpr int TILE_BYTES = BN * ROWB;
@@ -114,17 +117,23 @@ struct PPTile {
     static constexpr int DSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
     static constexpr int KSTEPS = BN / 16;
+    static constexpr int NKB = BN / 32;                // 32-key blocks per tile
+    static constexpr int NBUF = PF + 1;                // K and V buffers
+    static constexpr int NEB = PF + 2;                 // horizon buffers
     static constexpr int K_OFF = 0;
-    static constexpr int V_OFF = 3 * TILE_BYTES;
-    static constexpr int E_OFF = 6 * TILE_BYTES;
-    static constexpr int LDS_BYTES = E_OFF + 4 * BN * 4;
+    static constexpr int V_OFF = NBUF * TILE_BYTES;
+    static constexpr int E_OFF = 2 * NBUF * TILE_BYTES;
+    static constexpr int LDS_BYTES = E_OFF + NEB * BN * 4;
+    static_assert(NI >= 1 && BN % 64 == 0, "tile shape");
+    static_assert(PF == 2, "the tile loop issues loads two iterations ahead");
 };
 
-template <int D>
+template <int D, int BN_, int PF_>
 __global__ void __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_pp_kernel(const LaunchArgs args) {
-    using TT = PPTile<D>;
+    using TT = PPTile<D, BN_, PF_>;
     constexpr int BN = TT::BN;
+    constexpr int PF = TT::PF;
     constexpr int CPR = TT::CPR;
     constexpr int ROWB = TT::ROWB;
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -196,19 +205,24 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
 #pragma unroll
         for (int i = 0; i < TT::NI; ++i) dma_b128(rsrc, voffs[i] + tile_bytes, lds_addr(dst + (i * 8 + wave) * 1024));
     };
+    // horizons: waves 0 .. BN/64-1 each load 64 of the tile's entries
     auto issue_e = [&](int tile, lds_byte* dst) {
-        if (wave == 0) dma_b32(e_rsrc, (J.kbase + J.kstride * (tile * BN + lane)) * 4, lds_addr(dst));
+        if (wave < BN / 64)
+            dma_b32(e_rsrc, (J.kbase + J.kstride * (tile * BN + wave * 64 + lane)) * 4, lds_addr(dst + wave * 256));
     };
-    auto kbuf = [&](int s) { return lds + TT::K_OFF + (s % 3) * TT::TILE_BYTES; };
-    auto vbuf = [&](int s) { return lds + TT::V_OFF + (s % 3) * TT::TILE_BYTES; };
-    auto ebuf = [&](int s) { return lds + TT::E_OFF + (s & 3) * BN * 4; };
+    auto kbuf = [&](int s) { return lds + TT::K_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
+    auto vbuf = [&](int s) { return lds + TT::V_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
+    auto ebuf = [&](int s) { return lds + TT::E_OFF + (s % TT::NEB) * BN * 4; };
     // Wait until at most `pending` of this wave's vector-memory loads are in
-    // flight (vmcnt only; the immediate leaves expcnt and lgkmcnt unwaited).
+    // flight (vmcnt only; the immediate leaves expcnt and lgkmcnt unwaited):
+    // the largest immediate not above `pending` among the counts that occur.
     // Loads complete in issue order, so this waits for every older load.
     auto wait_older = [&](int pending) {
-        if (pending >= 2 * TT::NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * TT::NI + 1));
-        else if (pending >= 2 * TT::NI) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * TT::NI));
-        else if (pending >= TT::NI) __builtin_amdgcn_s_waitcnt(0xF70 | TT::NI);
+        constexpr int NI = TT::NI;
+        if (pending >= 2 * NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI + 1));
+        else if (pending >= 2 * NI) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI));
+        else if (pending >= NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (NI + 1));
+        else if (pending >= NI) __builtin_amdgcn_s_waitcnt(0xF70 | NI);
         else __builtin_amdgcn_s_waitcnt(0xF70);
     };
 
@@ -231,18 +245,18 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     float m_run = -INFINITY;
     float l_run = 0.f;
     const float c2 = args.scale_log2;
-    f32x16 s[2];
+    f32x16 s[TT::NKB];
     bf16x8 pb[TT::KSTEPS];
 
     auto qk = [&](const lds_byte* kb_lds) {
-        s[0] = f32x16{};
-        s[1] = f32x16{};
 #pragma unroll
-        for (int ds = 0; ds < TT::DSTEPS; ++ds) {
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kb_lds + koff[ds]), qreg[ds], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kb_lds + 32 * ROWB + koff[ds]), qreg[ds], s[1], 0,
-                                                           0, 0);
-        }
+        for (int kb = 0; kb < TT::NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+        for (int ds = 0; ds < TT::DSTEPS; ++ds)
+#pragma unroll
+            for (int kb = 0; kb < TT::NKB; ++kb)
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kb_lds + kb * 32 * ROWB + koff[ds]), qreg[ds],
+                                                                s[kb], 0, 0, 0);
     };
     auto pv = [&](const lds_byte* v_lds) {
 #pragma unroll
@@ -262,32 +276,39 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     auto softmax_phase = [&](int tile, int full, const lds_byte* e_lds) {
         if (!full) {
             // key j (block index) is visible iff j <= jlim and, for trees,
-            // ypos < end[kpos(j)]; jl below is the key's index in the tile
+            // ypos < end[kpos(j)]; jl below is the key's index in the tile.
+            // Branch-free: one compare (two for trees) and a select per score.
             const int lim = jlim - tile * BN - 8 * g;
+            if (tree) {
+                const auto* ep = reinterpret_cast<const __attribute__((address_space(3))) int*>(e_lds) + 8 * g;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < TT::NKB; ++kb) {
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int jl0 = kb * 32 + hf * 16;   // + 8g, folded into lim
-                    int ends[8];
-                    if (tree) {
-                        const auto* ep =
-                            reinterpret_cast<const __attribute__((address_space(3))) int*>(e_lds) + jl0 + 8 * g;
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int jl0 = kb * 32 + hf * 16;   // + 8g, folded into lim and ep
+                        int ends[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) ends[e] = ep[e];
-                    }
+                        for (int e = 0; e < 8; ++e) ends[e] = ep[jl0 + e];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        bool vis = jl0 + e <= lim;
-                        if (tree) vis = vis && ypos < ends[e];
-                        s[kb][hf * 8 + e] = vis ? s[kb][hf * 8 + e] : -INFINITY;
+                        for (int e = 0; e < 8; ++e) {
+                            const bool vis = (jl0 + e <= lim) & (ypos < ends[e]);
+                            s[kb][hf * 8 + e] = vis ? s[kb][hf * 8 + e] : -INFINITY;
+                        }
                     }
                 }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < TT::NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int jl = kb * 32 + (i >> 3) * 16 + (i & 7);
+                        s[kb][i] = jl <= lim ? s[kb][i] : -INFINITY;
+                    }
             }
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < TT::NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
         mx = xhalf_max(mx) * c2;
@@ -302,7 +323,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < TT::NKB; ++kb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m_use));
@@ -326,7 +347,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         if (with_pv) {
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < TT::KSTEPS * TT::DBLK; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
@@ -334,7 +355,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         if (with_qk) {
             if (!with_pv) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < TT::NKB * TT::DSTEPS; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
