@@ -353,17 +353,17 @@ static int run_jobs(std::vector<JobArgs>& jobs, const cpattn_mask* m, int heads,
         a.heads = heads;
         a.scale_log2 = scale_log2;
         int n = 0;
-        int64_t max_qt = 0;
+        int64_t sum_qt = 0;
         for (size_t i = first; i < jobs.size() && n < kMaxJobs; ++i, ++n) {
             a.jobs[n] = jobs[i];
-            max_qt = std::max<int64_t>(max_qt, jobs[i].q_tiles);
+            sum_qt += jobs[i].q_tiles;
         }
         // work slots: see work_item() in attn_kernel.hpp
         a.heads_per_xcd = heads >= 8 ? (heads + 7) / 8 : 0;
-        const int64_t slots = a.heads_per_xcd > 0 ? 8 * (int64_t)a.heads_per_xcd * n * max_qt : (int64_t)heads * n * max_qt;
+        const int64_t slots = a.heads_per_xcd > 0 ? 8 * (int64_t)a.heads_per_xcd * sum_qt : (int64_t)heads * sum_qt;
         if (slots > INT32_MAX / 2) return fail(CPATTN_EUNSUPPORTED, "too many workgroups in one launch");
         a.n_jobs = n;
-        a.max_q_tiles = (int32_t)max_qt;
+        a.sum_q_tiles = (int32_t)sum_qt;
         a.total_wg = (int32_t)slots;
         int rc = launch_partial(a, dtype, d, st);
         if (rc != CPATTN_OK) return rc;

@@ -79,43 +79,42 @@ struct LaunchArgs {
     int32_t n_jobs;
     int32_t heads;
     int32_t total_wg;        // work slots = grid size (some slots may be empty)
-    int32_t max_q_tiles;     // largest q_tiles among the jobs
+    int32_t sum_q_tiles;     // sum of q_tiles over the jobs
     int32_t heads_per_xcd;   // ceil(heads / 8) with at least 8 heads, else 0
     float scale_log2;        // scale * log2(e)
 };
 
 // ---------------------------------------------------------------------------
 // Work slot of workgroup `bid` -> (job, head, q-tile), or false for an empty
-// slot.  Work items are ordered by q-tile rank counted from the heavy end
-// (rank 0 = a job's last q-tile, whose queries see the most keys), then job,
-// then head, so heavy items of every job start first.  Workgroups are
-// dispatched round-robin over the 8 XCDs (bid % 8).  With at least 8 heads,
-// XCD x runs, in that order, the items of the heads h with h % 8 == x: every
-// XCD gets the same share of every job (no XCD is left with only the light
-// job of a launch), and the q-tiles of one head, which read the same K/V, share
-// one L2.  With fewer heads the items go round-robin over the XCDs.
+// slot.  Workgroups are dispatched round-robin over the 8 XCDs (bid % 8).
+// With at least 8 heads, XCD x runs the heads h with h % 8 == x of every job:
+// every XCD gets the same share of every job, so no XCD is left with only the
+// light job of a launch.  Within an XCD the items run one (job, head) group
+// after another, the group's q-tiles heaviest (last) first, so the ~32
+// workgroups in flight on the XCD read the same head's K/V and share its L2.
+// With fewer heads the same group order is dealt round-robin over the XCDs.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool work_item(const LaunchArgs& a, int bid, int* job, int* head, int* qtile) {
-    int r, j, h;
-    if (a.heads_per_xcd > 0) {
-        const int x = bid & 7, p = bid >> 3;
-        const int per_rank = a.n_jobs * a.heads_per_xcd;
-        r = p / per_rank;
-        const int rem = p - r * per_rank;
-        j = rem / a.heads_per_xcd;
-        h = x + 8 * (rem - j * a.heads_per_xcd);
-    } else {
-        const int per_rank = a.n_jobs * a.heads;
-        r = bid / per_rank;
-        const int rem = bid - r * per_rank;
-        j = rem / a.heads;
-        h = rem - j * a.heads;
+    const bool by_xcd = a.heads_per_xcd > 0;
+    const int x = bid & 7;
+    int p = by_xcd ? (bid >> 3) : bid;
+    const int hg = by_xcd ? a.heads_per_xcd : a.heads;   // head groups per job seen by this slot stream
+    for (int j = 0; j < a.n_jobs; ++j) {
+        const int qt = a.jobs[j].q_tiles;
+        const int n = hg * qt;
+        if (p < n) {
+            const int hi = p / qt;
+            const int r = p - hi * qt;
+            const int h = by_xcd ? x + 8 * hi : hi;
+            if (h >= a.heads) return false;
+            *job = j;
+            *head = h;
+            *qtile = qt - 1 - r;
+            return true;
+        }
+        p -= n;
     }
-    if (j >= a.n_jobs || h >= a.heads || r >= a.jobs[j].q_tiles) return false;
-    *job = j;
-    *head = h;
-    *qtile = a.jobs[j].q_tiles - 1 - r;
-    return true;
+    return false;
 }
 
 // ---------------------------------------------------------------------------
