@@ -82,25 +82,32 @@ __device__ __forceinline__ u32x2 lds_tr4(const lds_byte* p) {
 
 // ---------------------------------------------------------------------------
 // Ping-pong kernel: one workgroup of 8 waves = 256 query rows.  Waves w and
-// w + 4 share a SIMD (the dispatcher places them so), and the two groups of
-// four waves run the per-tile work in alternating phases separated by
-// workgroup barriers:
+// w + 4 share a SIMD (the dispatcher places them so).  Per key tile each wave
+// has a matrix phase and a softmax phase:
 //
-//   phase M(t): P(t-1) V(t-1) and S(t) = K(t) Q^T      -> 32 MFMAs per wave
-//   phase V(t): mask, row max, exp, row sum of S(t)     -> vector ALU only
+//   M(t): P(t-1) V(t-1) and S(t) = K(t) Q^T      -> 32 MFMAs per wave
+//   V(t): mask, row max, exp, row sum of S(t)     -> vector ALU only
 //
-// group 0 runs M(0) V(0) M(1) V(1) ..., group 1 the same one phase later, so
-// every SIMD always holds one wave in an MFMA phase and one in a softmax
-// phase.  Loads run two iterations ahead: at barrier 2t (t = tile sequence
-// index) every wave issues its share of K(t+2), E(t+2) and V(t+1), and before
-// barrier 2t+2 it waits only for the loads it issued at barrier 2t-2, so a
-// tile's HBM/L2 latency is hidden behind two iterations of work (all
-// workgroups of a head walk the same tiles at about the same time, so most of
-// them wait on the same miss).  K and V rotate over 3 buffers, E over 4: a
-// load never overwrites data that a phase between its issue and its wait
-// reads.  (Wider key tiles would halve the barriers per key, but 128-key
-// scores and probabilities do not fit the 256 registers a wave has at two
-// waves per SIMD.)
+// After the workgroup barrier that opens iteration t (t = tile sequence
+// index), group 0 (waves 0-3) runs M(t) then V(t) and group 1 runs V(t-1)
+// then M(t), so each SIMD holds one wave in a matrix phase and one in a
+// softmax phase and the matrix cores stay fed while the other wave computes
+// exponentials.  There is one barrier per iteration: a second one between the
+// phases (forcing the alternation) made the second matrix phase of every
+// iteration markedly slower and cost ~15% per tile.
+//
+// Loads are issued in the softmax phases, so the matrix phases carry no load
+// or tile-walk work: in iteration t group 1 issues K(t+2) and E(t+2) and
+// group 0 issues V(t+1), each wave a quarter of the tile.  Before the barrier
+// that opens iteration t+1 every wave waits for its own older loads, leaving
+// in flight only the ones it issued in iteration t: a tile gets at least an
+// iteration and a half to arrive before a matrix phase reads it, which hides
+// the HBM/L2 latency (all workgroups of a head walk the same tiles at about
+// the same time, so most of them wait on the same miss).  K and V rotate over
+// 3 buffers, E over 4: every buffer a load overwrites was last read before
+// the barrier that precedes the load.  (Wider key tiles would halve the
+// barriers per key, but 128-key scores and probabilities do not fit the 256
+// registers a wave has at two waves per SIMD.)
 // ---------------------------------------------------------------------------
 constexpr int kPPThreads = 512;
 constexpr int kPPBM = 256;
@@ -112,7 +119,7 @@ struct PPTile {
     static constexpr int CPR = D / 8;
     static constexpr int ROWB = D * 2;
     static constexpr int TILE_BYTES = BN * ROWB;
-    static constexpr int NI = TILE_BYTES / 1024 / 8;   // 1 KB direct loads per wave per tile
+    static constexpr int NI = TILE_BYTES / 1024 / 4;   // 1 KB direct loads per wave per tile (4 waves load it)
     static constexpr int RPB = 1024 / ROWB;            // rows per 1 KB block
     static constexpr int DSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
@@ -183,7 +190,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     // register-budget comment of attn_bf16_kernel for the swizzles)
     const int lrow = lane / CPR;
     const int lslot = lane % CPR;
-    const int rmod = (wave * TT::RPB + lrow) % CPR;
+    const int rmod = (wave * TT::RPB + lrow) % CPR;   // same for wave and wave & 3 (4 * RPB % CPR == 0)
     const int voff_k = lrow * J.k_st * 2 + ((lslot ^ rmod) * 16);
     const int voff_v = lrow * J.v_st * 2 + ((lslot ^ ((4 * rmod) % CPR)) * 16);
     // The head's K and V blocks (and the horizon array) as whole buffers: the
@@ -193,22 +200,25 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     const i32x4 k_rsrc = sgpr_rsrc(kh, (J.n_k - 1) * J.k_st * 2 + D * 2);
     const i32x4 v_rsrc = sgpr_rsrc(vh, (J.n_k - 1) * J.v_st * 2 + D * 2);
     const i32x4 e_rsrc = sgpr_rsrc(args.mask.end, args.mask.n_pos * 4);
+    // a tile is loaded by the four waves of one group: wave w & 3 fills the
+    // 1 KB blocks b = 4i + (w & 3); the horizons by the group's first wave
+    const int wl = wave & 3;
     int voffk[TT::NI], voffv[TT::NI];
 #pragma unroll
     for (int i = 0; i < TT::NI; ++i) {
-        const int rows = (i * 8 + wave) * TT::RPB;   // first row of this wave's i-th 1 KB block
+        const int rows = (i * 4 + wl) * TT::RPB;   // first row of this wave's i-th 1 KB block
         voffk[i] = voff_k + rows * J.k_st * 2;
         voffv[i] = voff_v + rows * J.v_st * 2;
     }
     auto issue_kv = [&](const i32x4& rsrc, const int* voffs, int st, int tile, lds_byte* dst) {
         const int tile_bytes = tile * BN * st * 2;
 #pragma unroll
-        for (int i = 0; i < TT::NI; ++i) dma_b128(rsrc, voffs[i] + tile_bytes, lds_addr(dst + (i * 8 + wave) * 1024));
+        for (int i = 0; i < TT::NI; ++i) dma_b128(rsrc, voffs[i] + tile_bytes, lds_addr(dst + (i * 4 + wl) * 1024));
     };
-    // horizons: waves 0 .. BN/64-1 each load 64 of the tile's entries
+    // horizons: the group's first BN/64 waves each load 64 of the tile's entries
     auto issue_e = [&](int tile, lds_byte* dst) {
-        if (wave < BN / 64)
-            dma_b32(e_rsrc, (J.kbase + J.kstride * (tile * BN + wave * 64 + lane)) * 4, lds_addr(dst + wave * 256));
+        if (wl < BN / 64)
+            dma_b32(e_rsrc, (J.kbase + J.kstride * (tile * BN + wl * 64 + lane)) * 4, lds_addr(dst + wl * 256));
     };
     auto kbuf = [&](int s) { return lds + TT::K_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
     auto vbuf = [&](int s) { return lds + TT::V_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
@@ -219,9 +229,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     // Loads complete in issue order, so this waits for every older load.
     auto wait_older = [&](int pending) {
         constexpr int NI = TT::NI;
-        if (pending >= 2 * NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI + 1));
-        else if (pending >= 2 * NI) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI));
-        else if (pending >= NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (NI + 1));
+        if (pending >= NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (NI + 1));
         else if (pending >= NI) __builtin_amdgcn_s_waitcnt(0xF70 | NI);
         else __builtin_amdgcn_s_waitcnt(0xF70);
     };
@@ -363,14 +371,14 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     };
 
     // ---- phase loop ---------------------------------------------------------------
-    // Barrier 2t opens iteration t (tile sequence index t); group 0 runs
-    // M(t) = {P(t-1)V(t-1), S(t)} then, after barrier 2t+1, V(t) = softmax(t);
-    // group 1 runs V(t-1) then M(t).  The first (no P V) and last (no S, no
-    // softmax for group 0) iterations are peeled so the steady-state body has
-    // no conditional work, and each group runs its own copy of the loop so
-    // that its loop-carried registers are allocated once (the G loop is fully
-    // unrolled; each copy serves one group).  Every wave passes
-    // the same barriers.
+    // Iteration t (tile sequence index t): group 0 runs M(t) = {P(t-1)V(t-1),
+    // S(t)} then V(t) = softmax(t); group 1 runs V(t-1) then M(t).  The first
+    // (no P V; barriers on both sides of the first matrix phase) and last (no
+    // S, no softmax for group 0) iterations are peeled so the steady-state
+    // body has no conditional work, and each group runs its own copy of the
+    // loop so that its loop-carried registers are allocated once (the G loop is
+    // fully unrolled; each copy serves one group).  Every wave passes the same
+    // barriers.
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
         if (group != G) continue;
@@ -380,69 +388,80 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         int t_cur = 0, f_cur = 0, t_nxt = 0, f_nxt = 0, t_n2 = 0, f_n2 = 0;
         if (!cur.next(J, args.mask, y0, y1, &t_cur, &f_cur)) break;   // tile 0
         bool h_nxt = cur.next(J, args.mask, y0, y1, &t_nxt, &f_nxt);
-        bool h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
-        const int e_loads = (tree && wave == 0) ? 1 : 0;   // horizon loads per tile of this wave
-        // prologue: K(0), E(0), then K(1), E(1), V(0), which may stay in flight
-        issue_kv(k_rsrc, voffk, J.k_st, t_cur, kbuf(0));
-        if (tree) issue_e(t_cur, ebuf(0));
-        if (h_nxt) {
-            issue_kv(k_rsrc, voffk, J.k_st, t_nxt, kbuf(1));
-            if (tree) issue_e(t_nxt, ebuf(1));
+        bool h_n2 = false;
+        // horizon loads per tile of this wave (group 1 loads them)
+        const int e_loads = (G == 1 && tree && wl < BN / 64) ? 1 : 0;
+        int pending;
+        // prologue: group 1 loads K(0), E(0), K(1), E(1), group 0 loads V(0);
+        // only K(0) and E(0) must land before barrier 0
+        if (G == 1) {
+            issue_kv(k_rsrc, voffk, J.k_st, t_cur, kbuf(0));
+            if (tree) issue_e(t_cur, ebuf(0));
+            if (h_nxt) {
+                issue_kv(k_rsrc, voffk, J.k_st, t_nxt, kbuf(1));
+                if (tree) issue_e(t_nxt, ebuf(1));
+            }
+            wait_older(h_nxt ? TT::NI + e_loads : 0);
+        } else {
+            issue_kv(v_rsrc, voffv, J.v_st, t_cur, vbuf(0));
         }
-        issue_kv(v_rsrc, voffv, J.v_st, t_cur, vbuf(0));
-        wait_older((h_nxt ? TT::NI + e_loads : 0) + TT::NI);
         phase_barrier();                                                // barrier 0
-        if (h_n2) {
-            issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(2));
-            if (tree) issue_e(t_n2, ebuf(2));
-        }
-        if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(1));
-        int pending = (h_n2 ? TT::NI + e_loads : 0) + (h_nxt ? TT::NI : 0);
         if (G == 0) {
             qk(kbuf(0));
             m_schedule(false, true);
             phase_barrier();                                            // barrier 1
+            if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(1));
+            pending = h_nxt ? TT::NI : 0;                               // V(1) may stay in flight
             softmax_phase(t_cur, f_cur, ebuf(0));
+            h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
         } else {
+            h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+            if (h_n2) {
+                issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(2));
+                if (tree) issue_e(t_n2, ebuf(2));
+            }
+            pending = h_n2 ? TT::NI + e_loads : 0;                      // K(2), E(2) may stay in flight
             phase_barrier();                                            // barrier 1
             qk(kbuf(0));
             m_schedule(false, true);
         }
         int t = 1;
         while (h_nxt) {
+            // iteration t: tile t (= t_nxt) exists; t_n2 / h_n2 describe tile t+1
             const int t_prev = t_cur, f_prev = f_cur;
             t_cur = t_nxt;
             f_cur = f_nxt;
             t_nxt = t_n2;
             f_nxt = f_n2;
             h_nxt = h_n2;
-            h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
             wait_older(pending);                                        // K(t), E(t), V(t-1) landed
-            phase_barrier();                                            // barrier 2t
-            if (h_n2) {
-                issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(t + 2));
-                if (tree) issue_e(t_n2, ebuf(t + 2));
-            }
-            if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(t + 1));
-            pending = (h_n2 ? TT::NI + e_loads : 0) + (h_nxt ? TT::NI : 0);
+            phase_barrier();                                            // opens iteration t
             if (G == 0) {
                 pv(vbuf(t - 1));
                 qk(kbuf(t));
                 m_schedule(true, true);
-                phase_barrier();                                        // barrier 2t+1
+                __builtin_amdgcn_sched_barrier(0);                      // phase boundary
+                if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(t + 1));
+                pending = h_nxt ? TT::NI : 0;
                 softmax_phase(t_cur, f_cur, ebuf(t));
+                h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
             } else {
+                h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+                if (h_n2) {
+                    issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(t + 2));
+                    if (tree) issue_e(t_n2, ebuf(t + 2));
+                }
+                pending = h_n2 ? TT::NI + e_loads : 0;
                 softmax_phase(t_prev, f_prev, ebuf(t - 1));
-                phase_barrier();                                        // barrier 2t+1
+                __builtin_amdgcn_sched_barrier(0);                      // phase boundary
                 pv(vbuf(t - 1));
                 qk(kbuf(t));
                 m_schedule(true, true);
             }
             ++t;
         }
-        // last iteration t = T: only tile T-1 (= cur) remains; nothing is in flight
-        // but V(T-1) (pending is 0 after the iteration that had no next tile)
-        wait_older(pending);
+        // last iteration t = T: only tile T-1 (= cur) remains; nothing is left in flight
+        wait_older(0);
         phase_barrier();                                                // barrier 2T
         if (G == 0) {
             pv(vbuf(t - 1));
