@@ -150,9 +150,12 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     ji = wave_uniform(ji);
     head = wave_uniform(head);
     qtile = wave_uniform(qtile);
-    // a copy, so that the fields the tile loop uses stay in scalar registers
-    // instead of being reloaded from the kernel arguments at every tile
-    const JobArgs J = args.jobs[ji];
+    // the few job fields the tile loop uses are copied to scalar registers;
+    // the rest is read from the kernel arguments where needed (copying the
+    // whole descriptor spilled scalar registers into vector lanes)
+    const JobArgs& J = args.jobs[ji];
+    const KeyBlock kblk{J.kbase, J.kstride, J.n_k};
+    const int k_st = J.k_st, v_st = J.v_st;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -218,7 +221,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     // horizons: the group's first BN/64 waves each load 64 of the tile's entries
     auto issue_e = [&](int tile, lds_byte* dst) {
         if (wl < BN / 64)
-            dma_b32(e_rsrc, (J.kbase + J.kstride * (tile * BN + wl * 64 + lane)) * 4, lds_addr(dst + wl * 256));
+            dma_b32(e_rsrc, (kblk.kbase + kblk.kstride * (tile * BN + wl * 64 + lane)) * 4, lds_addr(dst + wl * 256));
     };
     auto kbuf = [&](int s) { return lds + TT::K_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
     auto vbuf = [&](int s) { return lds + TT::V_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
@@ -383,11 +386,11 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     for (int G = 0; G < 2; ++G) {
         if (group != G) continue;
         TileCursor<BN> cur;
-        cur.init(J, args.mask, y0, y1);
+        cur.init(kblk, args.mask, y0, y1);
         // tiles t, t+1, t+2 of the walk (h_*: whether they exist)
         int t_cur = 0, f_cur = 0, t_nxt = 0, f_nxt = 0, t_n2 = 0, f_n2 = 0;
-        if (!cur.next(J, args.mask, y0, y1, &t_cur, &f_cur)) break;   // tile 0
-        bool h_nxt = cur.next(J, args.mask, y0, y1, &t_nxt, &f_nxt);
+        if (!cur.next(kblk, args.mask, y0, y1, &t_cur, &f_cur)) break;   // tile 0
+        bool h_nxt = cur.next(kblk, args.mask, y0, y1, &t_nxt, &f_nxt);
         bool h_n2 = false;
         // horizon loads per tile of this wave (group 1 loads them)
         const int e_loads = (G == 1 && tree && wl < BN / 64) ? 1 : 0;
@@ -395,29 +398,29 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         // prologue: group 1 loads K(0), E(0), K(1), E(1), group 0 loads V(0);
         // only K(0) and E(0) must land before barrier 0
         if (G == 1) {
-            issue_kv(k_rsrc, voffk, J.k_st, t_cur, kbuf(0));
+            issue_kv(k_rsrc, voffk, k_st, t_cur, kbuf(0));
             if (tree) issue_e(t_cur, ebuf(0));
             if (h_nxt) {
-                issue_kv(k_rsrc, voffk, J.k_st, t_nxt, kbuf(1));
+                issue_kv(k_rsrc, voffk, k_st, t_nxt, kbuf(1));
                 if (tree) issue_e(t_nxt, ebuf(1));
             }
             wait_older(h_nxt ? TT::NI + e_loads : 0);
         } else {
-            issue_kv(v_rsrc, voffv, J.v_st, t_cur, vbuf(0));
+            issue_kv(v_rsrc, voffv, v_st, t_cur, vbuf(0));
         }
         phase_barrier();                                                // barrier 0
         if (G == 0) {
             qk(kbuf(0));
             m_schedule(false, true);
             phase_barrier();                                            // barrier 1
-            if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(1));
+            if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(1));
             pending = h_nxt ? TT::NI : 0;                               // V(1) may stay in flight
             softmax_phase(t_cur, f_cur, ebuf(0));
-            h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+            h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
         } else {
-            h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+            h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
             if (h_n2) {
-                issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(2));
+                issue_kv(k_rsrc, voffk, k_st, t_n2, kbuf(2));
                 if (tree) issue_e(t_n2, ebuf(2));
             }
             pending = h_n2 ? TT::NI + e_loads : 0;                      // K(2), E(2) may stay in flight
@@ -441,14 +444,14 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                 qk(kbuf(t));
                 m_schedule(true, true);
                 __builtin_amdgcn_sched_barrier(0);                      // phase boundary
-                if (h_nxt) issue_kv(v_rsrc, voffv, J.v_st, t_nxt, vbuf(t + 1));
+                if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(t + 1));
                 pending = h_nxt ? TT::NI : 0;
                 softmax_phase(t_cur, f_cur, ebuf(t));
-                h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+                h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
             } else {
-                h_n2 = h_nxt && cur.next(J, args.mask, y0, y1, &t_n2, &f_n2);
+                h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
                 if (h_n2) {
-                    issue_kv(k_rsrc, voffk, J.k_st, t_n2, kbuf(t + 2));
+                    issue_kv(k_rsrc, voffk, k_st, t_n2, kbuf(t + 2));
                     if (tree) issue_e(t_n2, ebuf(t + 2));
                 }
                 pending = h_n2 ? TT::NI + e_loads : 0;

@@ -217,6 +217,12 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // visited through a later range is not visited again.  All state is
 // wave-uniform (scalar registers).
 // ---------------------------------------------------------------------------
+// The key block's position map and size: what the tile walk needs of a job
+// (kept apart so that the walk's state fits in a few scalar registers).
+struct KeyBlock {
+    int32_t kbase, kstride, n_k;
+};
+
 template <int BN>
 struct TileCursor {
     int t;           // next tile to emit (descending)
@@ -231,7 +237,7 @@ struct TileCursor {
     __device__ __forceinline__ static int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
     // Key index range of the positions [pa, pb] inside the block; false if empty.
-    __device__ __forceinline__ bool set_range(int pa, int pb, const JobArgs& J) {
+    __device__ __forceinline__ bool set_range(int pa, int pb, const KeyBlock& J) {
         int lo, hi;
         if (J.kstride == 1) {
             lo = pa - J.kbase;
@@ -250,7 +256,7 @@ struct TileCursor {
         return true;
     }
 
-    __device__ void init(const JobArgs& J, const MaskArgs& M, int y0, int y1) {
+    __device__ void init(const KeyBlock& J, const MaskArgs& M, int y0, int y1) {
         visited_lo = 0x7fffffff;
         own = 1;
         t = -1;
@@ -268,7 +274,7 @@ struct TileCursor {
     }
 
     // Produces the next tile; returns false when the walk is over.
-    __device__ bool next(const JobArgs& J, const MaskArgs& M, int y0, int y1, int* tile, int* full) {
+    __device__ bool next(const KeyBlock& J, const MaskArgs& M, int y0, int y1, int* tile, int* full) {
         while (t < t_lo || t < 0) {
             // current range exhausted: move to the parent segment's run
             if (seg < 0) return false;
@@ -365,6 +371,7 @@ partial_attention_kernel(const LaunchArgs args) {
     head = wave_uniform(head);
     qtile = wave_uniform(qtile);
     const JobArgs& J = args.jobs[ji];
+    const KeyBlock kblk{J.kbase, J.kstride, J.n_k};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -491,9 +498,9 @@ partial_attention_kernel(const LaunchArgs args) {
 
     // ---- tile walk ------------------------------------------------------------
     TileCursor<BN> cur;
-    cur.init(J, args.mask, y0, y1);
+    cur.init(kblk, args.mask, y0, y1);
     int tile, full;
-    bool have = cur.next(J, args.mask, y0, y1, &tile, &full);
+    bool have = cur.next(kblk, args.mask, y0, y1, &tile, &full);
     if (have) stage_load(tile);
     int buf = 0;
     const float c2 = args.scale_log2;
@@ -502,7 +509,7 @@ partial_attention_kernel(const LaunchArgs args) {
         stage_store(buf);
         __syncthreads();
         int ntile, nfull;
-        const bool nhave = cur.next(J, args.mask, y0, y1, &ntile, &nfull);
+        const bool nhave = cur.next(kblk, args.mask, y0, y1, &ntile, &nfull);
         if (nhave) stage_load(ntile);
 
         const T* Ks = reinterpret_cast<const T*>(smem + buf * TL::STAGE_BYTES);
