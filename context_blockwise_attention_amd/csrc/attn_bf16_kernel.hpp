@@ -96,16 +96,20 @@ __device__ __forceinline__ u32x2 lds_tr4(const lds_byte* p) {
 // phases (forcing the alternation) made the second matrix phase of every
 // iteration markedly slower and cost ~15% per tile.
 //
-// Loads are issued in the softmax phases, so the matrix phases carry no load
-// or tile-walk work: in iteration t group 1 issues K(t+2) and E(t+2) and
-// group 0 issues V(t+1), each wave a quarter of the tile.  Before the barrier
-// that opens iteration t+1 every wave waits for its own older loads, leaving
-// in flight only the ones it issued in iteration t: a tile gets at least an
-// iteration and a half to arrive before a matrix phase reads it, which hides
-// the HBM/L2 latency (all workgroups of a head walk the same tiles at about
-// the same time, so most of them wait on the same miss).  K and V rotate over
-// 3 buffers, E over 4: every buffer a load overwrites was last read before
-// the barrier that precedes the load.  (Wider key tiles would halve the
+// Group 0 issues every load, in its softmax phase: V(t+1) as the phase
+// opens, K(t+2) and E(t+2) once its tile walk has produced tile t+2; each
+// wave loads a quarter of a tile.  Group 0's half of an iteration is the
+// shorter one (it reaches the next barrier well before group 1), while group
+// 1's softmax phase leads into the second matrix phase of the iteration and
+// lies on the critical path, so it carries neither loads nor their address
+// and LDS-destination arithmetic.  Before the barrier that opens iteration
+// t+1 the loading waves wait for their own older loads, leaving in flight
+// only the ones issued in iteration t: a tile gets about an iteration and a
+// half to arrive before a matrix phase reads it, which hides the HBM/L2
+// latency (all workgroups of a head walk the same tiles at about the same
+// time, so most of them wait on the same miss).  K and V rotate over 3
+// buffers, E over 4: every buffer a load overwrites was last read before the
+// barrier that precedes the load.  (Wider key tiles would halve the
 // barriers per key, but 128-key scores and probabilities do not fit the 256
 // registers a wave has at two waves per SIMD.)
 // ---------------------------------------------------------------------------
@@ -203,8 +207,8 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     const i32x4 k_rsrc = sgpr_rsrc(kh, (J.n_k - 1) * J.k_st * 2 + D * 2);
     const i32x4 v_rsrc = sgpr_rsrc(vh, (J.n_k - 1) * J.v_st * 2 + D * 2);
     const i32x4 e_rsrc = sgpr_rsrc(args.mask.end, args.mask.n_pos * 4);
-    // a tile is loaded by the four waves of one group: wave w & 3 fills the
-    // 1 KB blocks b = 4i + (w & 3); the horizons by the group's first wave
+    // a tile is loaded by the four waves of group 0: wave w fills the 1 KB
+    // blocks b = 4i + w; the horizons by its first wave
     const int wl = wave & 3;
     int voffk[TT::NI], voffv[TT::NI];
 #pragma unroll
@@ -228,11 +232,14 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     auto ebuf = [&](int s) { return lds + TT::E_OFF + (s % TT::NEB) * BN * 4; };
     // Wait until at most `pending` of this wave's vector-memory loads are in
     // flight (vmcnt only; the immediate leaves expcnt and lgkmcnt unwaited):
-    // the largest immediate not above `pending` among the counts that occur.
-    // Loads complete in issue order, so this waits for every older load.
+    // the largest immediate not above `pending` among the counts that occur
+    // (one tile of V, K and E, or V alone).  Loads complete in issue order, so
+    // this waits for every older load.
     auto wait_older = [&](int pending) {
         constexpr int NI = TT::NI;
-        if (pending >= NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (NI + 1));
+        static_assert(2 * NI + 1 < 16, "vmcnt immediate");
+        if (pending >= 2 * NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI + 1));
+        else if (pending >= 2 * NI) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI));
         else if (pending >= NI) __builtin_amdgcn_s_waitcnt(0xF70 | NI);
         else __builtin_amdgcn_s_waitcnt(0xF70);
     };
@@ -325,6 +332,9 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         mx = xhalf_max(mx) * c2;
         const bool raise = mx > m_run + kTau;
         if (__builtin_amdgcn_ballot_w64(raise)) {
+            // rare: keeps the compiler from speculating the 64 accumulator
+            // multiplies (by 1) into every tile
+            __builtin_amdgcn_sched_barrier(0);
             const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
             l_run *= alpha;
 #pragma unroll
@@ -350,6 +360,16 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     auto phase_barrier = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The two waves of a SIMD are in opposite phases.  The one in its matrix
+    // phase runs at raised issue priority so that its MFMAs and operand reads
+    // go out as soon as they are ready, and the other wave's softmax fills
+    // the gaps (without it the older wave wins every conflict).
+    auto matrix_priority = [&](bool on) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (on) __builtin_amdgcn_s_setprio(3);
+        else __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     };
     // M phase schedule: LDS operand reads run ahead of the MFMAs that use
@@ -392,21 +412,23 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         if (!cur.next(kblk, args.mask, y0, y1, &t_cur, &f_cur)) break;   // tile 0
         bool h_nxt = cur.next(kblk, args.mask, y0, y1, &t_nxt, &f_nxt);
         bool h_n2 = false;
-        // horizon loads per tile of this wave (group 1 loads them)
-        const int e_loads = (G == 1 && tree && wl < BN / 64) ? 1 : 0;
-        int pending;
-        // prologue: group 1 loads K(0), E(0), K(1), E(1), group 0 loads V(0);
-        // only K(0) and E(0) must land before barrier 0
-        if (G == 1) {
-            issue_kv(k_rsrc, voffk, k_st, t_cur, kbuf(0));
-            if (tree) issue_e(t_cur, ebuf(0));
-            if (h_nxt) {
-                issue_kv(k_rsrc, voffk, k_st, t_nxt, kbuf(1));
-                if (tree) issue_e(t_nxt, ebuf(1));
-            }
-            wait_older(h_nxt ? TT::NI + e_loads : 0);
-        } else {
+        // horizon loads per tile of this wave (group 0 loads them)
+        const int e_loads = (G == 0 && tree && wl < BN / 64) ? 1 : 0;
+        // this wave's loads issued in the current iteration (they may stay in
+        // flight across the next barrier)
+        int pending = 0;
+        // K/E of tile t+2 (group 0, after its tile walk has produced it)
+        auto issue_ke = [&](int tile, int s) {
+            issue_kv(k_rsrc, voffk, k_st, tile, kbuf(s));
+            if (tree) issue_e(tile, ebuf(s));
+        };
+        // prologue: group 0 loads K(0), E(0), V(0), K(1), E(1); only K(0) and
+        // E(0) must land before barrier 0
+        if (G == 0) {
+            issue_ke(t_cur, 0);
             issue_kv(v_rsrc, voffv, v_st, t_cur, vbuf(0));
+            if (h_nxt) issue_ke(t_nxt, 1);
+            wait_older(TT::NI + (h_nxt ? TT::NI + e_loads : 0));
         }
         phase_barrier();                                                // barrier 0
         if (G == 0) {
@@ -414,16 +436,12 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             m_schedule(false, true);
             phase_barrier();                                            // barrier 1
             if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(1));
-            pending = h_nxt ? TT::NI : 0;                               // V(1) may stay in flight
             softmax_phase(t_cur, f_cur, ebuf(0));
             h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
+            if (h_n2) issue_ke(t_n2, 2);
+            pending = (h_nxt ? TT::NI : 0) + (h_n2 ? TT::NI + e_loads : 0);   // V(1), K(2), E(2)
         } else {
             h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
-            if (h_n2) {
-                issue_kv(k_rsrc, voffk, k_st, t_n2, kbuf(2));
-                if (tree) issue_e(t_n2, ebuf(2));
-            }
-            pending = h_n2 ? TT::NI + e_loads : 0;                      // K(2), E(2) may stay in flight
             phase_barrier();                                            // barrier 1
             qk(kbuf(0));
             m_schedule(false, true);
@@ -440,26 +458,24 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             wait_older(pending);                                        // K(t), E(t), V(t-1) landed
             phase_barrier();                                            // opens iteration t
             if (G == 0) {
+                matrix_priority(true);
                 pv(vbuf(t - 1));
                 qk(kbuf(t));
                 m_schedule(true, true);
-                __builtin_amdgcn_sched_barrier(0);                      // phase boundary
+                matrix_priority(false);                                 // phase boundary
                 if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(t + 1));
-                pending = h_nxt ? TT::NI : 0;
                 softmax_phase(t_cur, f_cur, ebuf(t));
                 h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
+                if (h_n2) issue_ke(t_n2, t + 2);
+                pending = (h_nxt ? TT::NI : 0) + (h_n2 ? TT::NI + e_loads : 0);
             } else {
                 h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
-                if (h_n2) {
-                    issue_kv(k_rsrc, voffk, k_st, t_n2, kbuf(t + 2));
-                    if (tree) issue_e(t_n2, ebuf(t + 2));
-                }
-                pending = h_n2 ? TT::NI + e_loads : 0;
                 softmax_phase(t_prev, f_prev, ebuf(t - 1));
-                __builtin_amdgcn_sched_barrier(0);                      // phase boundary
+                matrix_priority(true);                                  // phase boundary
                 pv(vbuf(t - 1));
                 qk(kbuf(t));
                 m_schedule(true, true);
+                matrix_priority(false);
             }
             ++t;
         }
