@@ -32,7 +32,6 @@ __device__ __forceinline__ bf16x8 lds_op(const lds_byte* p) {
 }
 // Raw buffer descriptor (base, stride 0, size in bytes, the flags of
 // make_rsrc) as four scalar registers, for the inline-asm loads below.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, int32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     i32x4 r;
@@ -409,8 +408,8 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         cur.init(kblk, args.mask, y0, y1);
         // tiles t, t+1, t+2 of the walk (h_*: whether they exist)
         int t_cur = 0, f_cur = 0, t_nxt = 0, f_nxt = 0, t_n2 = 0, f_n2 = 0;
-        if (!cur.next(kblk, args.mask, y0, y1, &t_cur, &f_cur)) break;   // tile 0
-        bool h_nxt = cur.next(kblk, args.mask, y0, y1, &t_nxt, &f_nxt);
+        if (!cur.next(kblk, args.mask, y1, &t_cur, &f_cur)) break;   // tile 0
+        bool h_nxt = cur.next(kblk, args.mask, y1, &t_nxt, &f_nxt);
         bool h_n2 = false;
         // horizon loads per tile of this wave (group 0 loads them)
         const int e_loads = (G == 0 && tree && wl < BN / 64) ? 1 : 0;
@@ -437,11 +436,11 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             phase_barrier();                                            // barrier 1
             if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(1));
             softmax_phase(t_cur, f_cur, ebuf(0));
-            h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
+            h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
             if (h_n2) issue_ke(t_n2, 2);
             pending = (h_nxt ? TT::NI : 0) + (h_n2 ? TT::NI + e_loads : 0);   // V(1), K(2), E(2)
         } else {
-            h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
+            h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
             phase_barrier();                                            // barrier 1
             qk(kbuf(0));
             m_schedule(false, true);
@@ -465,11 +464,11 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                 matrix_priority(false);                                 // phase boundary
                 if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(t + 1));
                 softmax_phase(t_cur, f_cur, ebuf(t));
-                h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
+                h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
                 if (h_n2) issue_ke(t_n2, t + 2);
                 pending = (h_nxt ? TT::NI : 0) + (h_n2 ? TT::NI + e_loads : 0);
             } else {
-                h_n2 = h_nxt && cur.next(kblk, args.mask, y0, y1, &t_n2, &f_n2);
+                h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
                 softmax_phase(t_prev, f_prev, ebuf(t - 1));
                 matrix_priority(true);                                  // phase boundary
                 pv(vbuf(t - 1));

@@ -223,21 +223,33 @@ struct KeyBlock {
     int32_t kbase, kstride, n_k;
 };
 
+// Segment-table entry, read through the scalar cache (the index is
+// wave-uniform and the table is constant for the launch).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 seg_entry(const MaskArgs& M, int s) {
+    return ((const __attribute__((address_space(4))) i32x4*)M.segtab)[s];
+}
+
+// Each range of key positions becomes a range of tiles [t_lo, t] (clipped
+// below the tiles already emitted), and the tiles [fa, fb] of it are full
+// (every key visible to every query row of the tile).  Both are decided once
+// per range, so producing a tile is a compare and a decrement; moving to the
+// next range is the rare path.
 template <int BN>
 struct TileCursor {
-    int t;           // next tile to emit (descending)
-    int t_lo;        // lowest tile of the current range
-    int j_lo, j_hi;  // current range in key indices, inclusive
-    int visited_lo;  // lowest tile emitted so far
-    int seg;         // segment whose run is the current range (tree); -1 = done
-    int own;         // current range is the query tile's own range
-    int full_ok;     // every key of the current range is visible to every query row
+    int t;        // next tile to emit; the range is exhausted when t < t_lo
+    int t_lo;     // lowest tile of the current range
+    int fa, fb;   // full tiles of the current range (none when fa > fb)
+    int seg;      // segment whose run is the current range (tree); -1 = no further range
 
     __device__ __forceinline__ static int ceil_div(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
     __device__ __forceinline__ static int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
-    // Key index range of the positions [pa, pb] inside the block; false if empty.
-    __device__ __forceinline__ bool set_range(int pa, int pb, const KeyBlock& J) {
+    // Enters the key positions [pa, pb] inside the block.  A tile is full if
+    // it lies inside the range, full_ok holds (every key's subtree contains
+    // the whole query tile) and its last key index is at most j_last.  False
+    // (state unchanged) if no tile below the ones emitted is left.
+    __device__ __forceinline__ bool set_range(int pa, int pb, bool full_ok, int j_last, const KeyBlock& J) {
         int lo, hi;
         if (J.kstride == 1) {
             lo = pa - J.kbase;
@@ -249,53 +261,51 @@ struct TileCursor {
         lo = max(lo, 0);
         hi = min(hi, J.n_k - 1);
         if (lo > hi) return false;
-        j_lo = lo;
-        j_hi = hi;
-        t_lo = lo / BN;
-        t = min(hi / BN, visited_lo - 1);
+        const int th = min(hi / BN, t);
+        const int tl = lo / BN;
+        if (th < tl) return false;
+        t = th;
+        t_lo = tl;
+        // tile u is full iff u*BN >= lo, u*BN + BN - 1 <= min(hi, j_last)
+        // (j_last + 1 <= 0 leaves fb < 0: no tile full)
+        fa = full_ok ? (lo + BN - 1) / BN : 1;
+        fb = full_ok ? min(hi + 1, j_last + 1) / BN - 1 : 0;
         return true;
     }
 
+    // The first range: the query tile's own run up to y1 (its keys after y0
+    // are not visible to the first query row: j_last is y0's key index).
     __device__ void init(const KeyBlock& J, const MaskArgs& M, int y0, int y1) {
-        visited_lo = 0x7fffffff;
-        own = 1;
-        t = -1;
-        t_lo = 0;
+        t = 0x7ffffffe;   // nothing emitted yet
+        t_lo = 0x7fffffff;
+        seg = -1;
+        const int j_own = J.kstride == 1 ? y0 - J.kbase : floor_div(y0 - J.kbase, J.kstride);
         if (M.kind == kCausal) {
-            seg = -1;
-            full_ok = 1;
-            set_range(0, y1, J);
+            set_range(0, y1, true, j_own, J);
             return;
         }
-        seg = wave_uniform(M.seg[y0]);
-        int4 st = M.segtab[seg];
-        full_ok = wave_uniform(st.w) > y1;
-        if (!set_range(wave_uniform(st.x), y1, J)) t = -1;
+        seg = ((const __attribute__((address_space(4))) int32_t*)M.seg)[y0];
+        const i32x4 st = seg_entry(M, seg);
+        set_range(st.x, y1, st.w > y1, j_own, J);
+    }
+
+    // Moves to the runs of the ancestor segments until one has a tile left.
+    __device__ bool advance(const KeyBlock& J, const MaskArgs& M, int y1) {
+        while (seg >= 0) {
+            seg = seg_entry(M, seg).z;
+            if (seg < 0) break;
+            const i32x4 sp = seg_entry(M, seg);
+            if (set_range(sp.x, sp.y - 1, sp.w > y1, 0x7ffffffe, J)) return true;
+        }
+        return false;
     }
 
     // Produces the next tile; returns false when the walk is over.
-    __device__ bool next(const KeyBlock& J, const MaskArgs& M, int y0, int y1, int* tile, int* full) {
-        while (t < t_lo || t < 0) {
-            // current range exhausted: move to the parent segment's run
-            if (seg < 0) return false;
-            int p = wave_uniform(M.segtab[seg].z);
-            seg = p;
-            if (p < 0) return false;
-            int4 sp = M.segtab[p];
-            own = 0;
-            full_ok = wave_uniform(sp.w) > y1;
-            if (!set_range(wave_uniform(sp.x), wave_uniform(sp.y) - 1, J)) t = -1;
-        }
-        const int tt = t;
+    __device__ __forceinline__ bool next(const KeyBlock& J, const MaskArgs& M, int y1, int* tile, int* full) {
+        if (t < t_lo && !advance(J, M, y1)) return false;
+        *tile = t;
+        *full = (t >= fa) & (t <= fb);
         --t;
-        visited_lo = tt;
-        // full iff the tile lies inside the range, is not ragged, every key
-        // precedes every query and every horizon passes y1
-        const int k0 = tt * BN, k1 = tt * BN + BN - 1;
-        int f = full_ok && k0 >= j_lo && k1 <= j_hi;
-        if (f && own) f = J.kbase + J.kstride * k1 <= y0;
-        *tile = wave_uniform(tt);
-        *full = wave_uniform(f);
         return true;
     }
 };
@@ -500,7 +510,7 @@ partial_attention_kernel(const LaunchArgs args) {
     TileCursor<BN> cur;
     cur.init(kblk, args.mask, y0, y1);
     int tile, full;
-    bool have = cur.next(kblk, args.mask, y0, y1, &tile, &full);
+    bool have = cur.next(kblk, args.mask, y1, &tile, &full);
     if (have) stage_load(tile);
     int buf = 0;
     const float c2 = args.scale_log2;
@@ -509,7 +519,7 @@ partial_attention_kernel(const LaunchArgs args) {
         stage_store(buf);
         __syncthreads();
         int ntile, nfull;
-        const bool nhave = cur.next(kblk, args.mask, y0, y1, &ntile, &nfull);
+        const bool nhave = cur.next(kblk, args.mask, y1, &ntile, &nfull);
         if (nhave) stage_load(ntile);
 
         const T* Ks = reinterpret_cast<const T*>(smem + buf * TL::STAGE_BYTES);
