@@ -96,6 +96,31 @@ def tree_visible_pairs(seg: np.ndarray, parent: np.ndarray, q_rows: np.ndarray) 
     return anc_len[s_of] + (q_rows - starts[s_of] + 1)
 
 
+def block_pair_counts(seg: np.ndarray, parent: np.ndarray, c: int, N: int) -> np.ndarray:
+    """Visible pairs [r, b] between the queries of contiguous block r and the
+    keys of block b (blocks of c positions), by integer arithmetic on the
+    segment runs: own-segment prefix plus every ancestor run."""
+    n_seg = len(parent)
+    first = np.flatnonzero(np.r_[True, seg[1:] != seg[:-1]])
+    starts = np.zeros(n_seg, dtype=np.int64)
+    ends = np.zeros(n_seg, dtype=np.int64)
+    starts[seg[first]] = first
+    ends[seg[first]] = np.r_[first[1:], len(seg)]
+    out = np.zeros((N, N), dtype=np.int64)
+    y = np.arange(len(seg), dtype=np.int64)
+    for b in range(N):
+        lo, hi = b * c, (b + 1) * c            # key positions [lo, hi)
+        def inside(a, e):                      # keys of [a, e) inside the block
+            return np.clip(np.minimum(e, hi) - np.maximum(a, lo), 0, None)
+        anc = np.zeros(n_seg, dtype=np.int64)
+        for s_ in range(n_seg):                # parents precede children
+            p_ = parent[s_]
+            anc[s_] = 0 if p_ < 0 else anc[p_] + inside(starts[p_], ends[p_])
+        per_row = anc[seg] + inside(starts[seg], y + 1)
+        out[:, b] = per_row.reshape(N, c).sum(axis=1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,8 +211,10 @@ def main():
     per = np.array([a.elapsed_time(b) for a, b in ev])
     ms = float(per.mean())
     tflops = flops / (ms * 1e-3) / 1e12
-    # launches of the partial kernel per step: one per non-empty round
-    launches = N   # every round of the contiguous tree split has work for some rank
+    # launches of the partial kernel per step: launch l holds every rank's l-th
+    # non-empty round, so there are as many as the busiest rank has rounds
+    pairs_rb = block_pair_counts(seg, parent, c, N)
+    launches = int((pairs_rb > 0).sum(axis=1).max())
     avg_launch_ms = ms / launches
 
     # standalone merge (materialised partials): rank N-1's 4 partials -> one

@@ -55,6 +55,7 @@ struct cpattn_mask {
     int32_t kind;                 // kCausal or kTree
     int64_t n_pos;
     std::vector<SegInfo> segs;    // host copy (tree)
+    std::vector<int32_t> run_order;   // segments by run start (tree)
     int32_t* d_seg = nullptr;     // [n_pos]
     int32_t* d_end = nullptr;     // [n_pos]
     int4* d_segtab = nullptr;     // [n_seg]
@@ -152,6 +153,7 @@ extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int3
     m->kind = kTree;
     m->n_pos = n_tok;
     m->segs = segs;
+    m->run_order = order;
     std::vector<int32_t> end((size_t)n_tok);
     for (int64_t x = 0; x < n_tok; ++x) end[x] = segs[seg_id[x]].subtree_end;
     std::vector<int4> tab((size_t)n_seg);
@@ -247,6 +249,41 @@ static bool pair_nonempty(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cp
         if (y <= qmax && y < s.subtree_end) return true;
     }
     return false;
+}
+
+// Number of keys of a block (positions base + stride * j, j < n) inside the
+// position range [a, b].
+static int64_t keys_in_range(cpattn_posmap kp, int64_t nk, int64_t a, int64_t b) {
+    if (a > b || nk == 0) return 0;
+    auto ceil_div = [](int64_t x, int64_t y) { return x >= 0 ? (x + y - 1) / y : -((-x) / y); };
+    auto floor_div = [](int64_t x, int64_t y) { return x >= 0 ? x / y : -((-x + y - 1) / y); };
+    const int64_t lo = std::max<int64_t>(0, ceil_div(a - kp.base, kp.stride));
+    const int64_t hi = std::min<int64_t>(nk - 1, floor_div(b - kp.base, kp.stride));
+    return hi >= lo ? hi - lo + 1 : 0;
+}
+
+// Approximate visible (query, key) pairs of a block pair, from about 256
+// evenly spaced query rows; used only to order the jobs of a launch.
+static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
+    if (nq == 0 || nk == 0) return 0.0;
+    const int64_t step = std::max<int64_t>(1, nq / 256);
+    double sum = 0.0;
+    for (int64_t i = 0; i < nq; i += step) {
+        const int64_t y = qp.base + qp.stride * i;
+        if (m->kind == kCausal) {
+            sum += (double)keys_in_range(kp, nk, 0, y);
+            continue;
+        }
+        // segment of position y: the last run starting at or before y
+        auto it = std::upper_bound(m->run_order.begin(), m->run_order.end(), y,
+                                   [&](int64_t v, int32_t seg) { return v < m->segs[seg].run_start; });
+        int32_t sg = *(it - 1);
+        int64_t c = keys_in_range(kp, nk, m->segs[sg].run_start, y);
+        for (int32_t a = m->segs[sg].parent; a >= 0; a = m->segs[a].parent)
+            c += keys_in_range(kp, nk, m->segs[a].run_start, m->segs[a].run_end - 1);
+        sum += (double)c;
+    }
+    return sum * (double)step;
 }
 
 // ---------------------------------------------------------------------------
@@ -473,20 +510,39 @@ extern "C" int cpattn_ring_emulate(int N, const cpattn_tensor* q_blocks, const c
     const int heads = (int)ref.n_heads;
     const int dtype = ref.dtype;
     const int d = (int)ref.d;
-    std::vector<char> written(N, 0);
-    for (int k = 0; k < N; ++k) {
-        std::vector<JobArgs> jobs;
-        for (int r : run) {
+    // Each rank's rounds in ring order (block (r - k) mod N in round k),
+    // without the empty ones.  Launch l runs the l-th non-empty round of every
+    // rank: the ranks are independent, and each rank's rounds still merge in
+    // ring order, so this is the ring's result with fewer, fuller launches.
+    std::vector<std::vector<int>> visits(N);
+    size_t n_launch = 0;
+    for (int r : run) {
+        for (int k = 0; k < N; ++k) {
             const int b = ((r - k) % N + N) % N;
-            if (!pair_nonempty(mask, pos[r], q_blocks[r].n_tok, pos[b], k_blocks[b].n_tok)) continue;
-            jobs.push_back(make_job(&q_blocks[r], &k_blocks[b], &v_blocks[b], pos[r], pos[b], o_out[r], lse_out[r],
-                                    written[r] ? 1 : 0));
-            written[r] = 1;
+            if (pair_nonempty(mask, pos[r], q_blocks[r].n_tok, pos[b], k_blocks[b].n_tok)) visits[r].push_back(b);
         }
-        if ((rc = run_jobs(jobs, mask, heads, scale, dtype, d, st))) return rc;
+        n_launch = std::max(n_launch, visits[r].size());
+    }
+    for (size_t l = 0; l < n_launch; ++l) {
+        std::vector<JobArgs> jobs;
+        std::vector<double> work;
+        for (int r : run) {
+            if (l >= visits[r].size()) continue;
+            const int b = visits[r][l];
+            jobs.push_back(make_job(&q_blocks[r], &k_blocks[b], &v_blocks[b], pos[r], pos[b], o_out[r], lse_out[r],
+                                    l > 0 ? 1 : 0));
+            work.push_back(pair_estimate(mask, pos[r], q_blocks[r].n_tok, pos[b], k_blocks[b].n_tok));
+        }
+        // heaviest job first: the launch's last workgroups are its lightest
+        std::vector<size_t> idx(jobs.size());
+        for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+        std::stable_sort(idx.begin(), idx.end(), [&](size_t x, size_t y) { return work[x] > work[y]; });
+        std::vector<JobArgs> sorted;
+        for (size_t i : idx) sorted.push_back(jobs[i]);
+        if ((rc = run_jobs(sorted, mask, heads, scale, dtype, d, st))) return rc;
     }
     for (int r : run)
-        if (!written[r] && (rc = launch_fill(o_out[r], lse_out[r], heads * q_blocks[r].n_tok, d, st))) return rc;
+        if (visits[r].empty() && (rc = launch_fill(o_out[r], lse_out[r], heads * q_blocks[r].n_tok, d, st))) return rc;
     return CPATTN_OK;
 }
 

@@ -340,25 +340,33 @@ __device__ __forceinline__ void write_result(const JobArgs& J, int head, int qi,
             }
         if (g == 0) *lrow = lse_new;
     } else {
+        // the running LSE and O are read together (one memory round trip)
+        f32x4 old[DBLK * 4];
         const float lse_old = *lrow;
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                old[b * 4 + q4] = *reinterpret_cast<const f32x4*>(orow + b * 32 + q4 * 8 + g * 4);
+        // Branch-free, so that the loads above are not sunk behind a test of
+        // the LSE: when both sides are empty (M = -inf) the weights are 0 and
+        // the row is rewritten as (0, -inf).
         const float M = fmaxf(lse_old, lse_new);
-        if (M == -INFINITY) return;   // both sides empty: keep (0, -inf)
-        const float wa = expf(lse_old - M), wb = expf(lse_new - M);
+        const bool none = M == -INFINITY;
+        const float wa = none ? 0.f : expf(lse_old - M), wb = none ? 0.f : expf(lse_new - M);
         const float z = wa + wb;
-        const float rz = 1.f / z;
+        const float rz = none ? 0.f : 1.f / z;
         const float wbn = wb * inv;
 #pragma unroll
         for (int b = 0; b < DBLK; ++b)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                f32x4* dst = reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4);
-                const f32x4 old = *dst;
                 f32x4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (wa * old[e] + wbn * acc[b][q4 * 4 + e]) * rz;
-                *dst = v;
+                for (int e = 0; e < 4; ++e) v[e] = (wa * old[b * 4 + q4][e] + wbn * acc[b][q4 * 4 + e]) * rz;
+                *reinterpret_cast<f32x4*>(orow + b * 32 + q4 * 8 + g * 4) = v;
             }
-        if (g == 0) *lrow = M + logf(z);
+        if (g == 0) *lrow = none ? -INFINITY : M + logf(z);
     }
 }
 

@@ -146,8 +146,10 @@ int cpattn_merge(int n_parts, const float* const* o_parts, const float* const* l
  * the partial of q_blocks[r] against the K/V block of rank (r - k) mod N and
  * merges it into o_out[r]/lse_out[r] (round 0 writes, later rounds merge).
  * Rounds in which no query of r sees any key of the visiting block are
- * skipped (their merge would be the identity).  All ranks' round k run in
- * one launch, as the ranks of a real ring run that round concurrently.
+ * skipped (their merge would be the identity).  The ranks are independent, so
+ * one launch runs the next non-empty round of every rank (as the ranks of a
+ * real ring run their rounds concurrently); each rank's rounds are still
+ * merged in ring order.
  *   q_blocks, k_blocks, v_blocks, pos: host arrays of N entries.
  *   o_out, lse_out: host arrays of N device pointers ([H][n_q_r][d] and
  *                   [H][n_q_r] fp32); entries of ranks not run may be NULL.
