@@ -74,7 +74,7 @@ def traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mi
     # one step = the last launches_per_step dispatches
     f_step = sum(f[-launches_per_step:]) * 1024.0 * k_fetch
     w_step = sum(w[-launches_per_step:]) * 1024.0 * k_write
-    return {"kernel": KERNEL_NAME, "source_hash": kernel_source_hash(),
+    return {"kernel": KERNEL_NAME, "source_hash": kernel_source_hash(), "launches_per_step": launches_per_step,
             "fetch_bytes_per_launch": f_step / launches_per_step,
             "write_bytes_per_launch": w_step / launches_per_step,
             "copy_factor_fetch": k_fetch, "copy_factor_write": k_write, "copy_mib": copy_mib}
@@ -136,7 +136,10 @@ def main():
                     help="write the traffic record from rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
     if args.traffic_from:
-        rec = traffic_record(*args.traffic_from, copy_mib=args.copy_mib or 1024, launches_per_step=args.blocks)
+        import workloads
+        seg, parent = workloads.tree_prompt_completions(24576, (8192,) * 5)
+        n_launch = int((block_pair_counts(seg, parent, len(seg) // args.blocks, args.blocks) > 0).sum(axis=1).max())
+        rec = traffic_record(*args.traffic_from, copy_mib=args.copy_mib or 1024, launches_per_step=n_launch)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
