@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
   optionally merged into a running (O, LSE).
 * :func:`merge` -- merge of several partials.
 * :func:`ring_emulate` -- every round of a ring of N ranks on one GPU.
+* :func:`ring_emulate_chunks` -- the same for ranks that hold several chunks
+  (the zig-zag layout).
+* :func:`ring_plan` -- per-rank, per-round visible-pair counts (host only).
 """
 from __future__ import annotations
 
@@ -71,8 +74,11 @@ def lib():
         L.cpattn_merge.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int64, P, P, P]
         L.cpattn_ring_emulate.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float,
                                           P, P, P]
+        L.cpattn_ring_emulate_chunks.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, P,
+                                                 ctypes.c_float, P, P, P]
+        L.cpattn_ring_plan.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P]
         for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
-                  "cpattn_merge", "cpattn_ring_emulate"):
+                  "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -254,3 +260,67 @@ def ring_emulate(q_blocks: Sequence[Optional[torch.Tensor]], k_blocks: Sequence[
                                      float(_default_scale(d) if scale is None else scale), op, lp,
                                      _stream(stream)))
     return {r: outs[r] for r in run}
+
+
+def ring_emulate_chunks(q_chunks: Sequence[Optional[torch.Tensor]], k_chunks: Sequence[torch.Tensor],
+                        v_chunks: Sequence[torch.Tensor], pos: Sequence[Tuple[int, int]], mask: Mask,
+                        chunks_per_rank: int, scale: Optional[float] = None, ranks: Optional[Sequence[int]] = None,
+                        outs=None, stream=None):
+    """Ring of N ranks holding ``chunks_per_rank`` (C) chunks each: chunk
+    ``r * C + c`` of rank r has queries ``q_chunks[i]``, keys/values
+    ``k_chunks[i]``/``v_chunks[i]`` at positions ``pos[i] = (base, stride)``.
+    In round k every chunk of rank r meets every key chunk of rank
+    ``(r - k) mod N``.  Returns ``{chunk index: (O, LSE)}`` for the chunks of
+    the ranks run."""
+    C = int(chunks_per_rank)
+    NC = len(k_chunks)
+    if C < 1 or NC % C != 0:
+        raise ValueError("the number of chunks must be a multiple of chunks_per_rank")
+    N = NC // C
+    if not (len(v_chunks) == len(pos) == len(q_chunks) == NC):
+        raise ValueError("every chunk needs q/k/v and positions")
+    run = list(range(N)) if ranks is None else [int(r) for r in ranks]
+    units = [r * C + c for r in run for c in range(C)]
+    d = k_chunks[0].shape[2]
+    H = k_chunks[0].shape[0]
+    if outs is None:
+        outs = {}
+        for i in units:
+            nq = q_chunks[i].shape[1]
+            outs[i] = (torch.empty((H, nq, d), dtype=torch.float32, device=k_chunks[0].device),
+                       torch.empty((H, nq), dtype=torch.float32, device=k_chunks[0].device))
+    for i in units:
+        o, l = outs[i]
+        nq = q_chunks[i].shape[1]
+        if o.shape != (H, nq, d) or l.shape != (H, nq) or o.dtype != torch.float32 or l.dtype != torch.float32 \
+                or not o.is_contiguous() or not l.is_contiguous():
+            raise ValueError("outs[%d] must be contiguous fp32 ([H, n_q, d], [H, n_q])" % i)
+    qd = (_Tensor * NC)(*[_desc(q_chunks[i] if i in outs else None, "q") for i in range(NC)])
+    kd = (_Tensor * NC)(*[_desc(k, "k") for k in k_chunks])
+    vd = (_Tensor * NC)(*[_desc(v, "v") for v in v_chunks])
+    pd = (_PosMap * NC)(*[_posmap(p) for p in pos])
+    rk = (ctypes.c_int * len(run))(*run)
+    op = (ctypes.c_void_p * NC)(*[(outs[i][0].data_ptr() if i in outs else None) for i in range(NC)])
+    lp = (ctypes.c_void_p * NC)(*[(outs[i][1].data_ptr() if i in outs else None) for i in range(NC)])
+    _check(lib().cpattn_ring_emulate_chunks(N, C, qd, kd, vd, pd, rk, len(run), mask.handle,
+                                            float(_default_scale(d) if scale is None else scale), op, lp,
+                                            _stream(stream)))
+    return {i: outs[i] for i in units}
+
+
+def ring_plan(n_tok: Sequence[int], pos: Sequence[Tuple[int, int]], mask: Mask, chunks_per_rank: int = 1):
+    """Visible (query, key) pairs per head of every rank in every round, as an
+    ``[N, N]`` int64 array: ``work[r, k]`` = rank r's pairs against the keys
+    of rank ``(r - k) mod N``.  Host-only; chunk i has ``n_tok[i]`` tokens at
+    ``pos[i]``."""
+    import numpy as np
+    C = int(chunks_per_rank)
+    NC = len(n_tok)
+    if C < 1 or NC % C != 0 or len(pos) != NC:
+        raise ValueError("n_tok and pos need N * chunks_per_rank entries")
+    N = NC // C
+    nt = (ctypes.c_int64 * NC)(*[int(x) for x in n_tok])
+    pd = (_PosMap * NC)(*[_posmap(p) for p in pos])
+    work = np.zeros(N * N, dtype=np.int64)
+    _check(lib().cpattn_ring_plan(N, C, nt, pd, mask.handle, work.ctypes.data))
+    return work.reshape(N, N)

@@ -262,16 +262,16 @@ static int64_t keys_in_range(cpattn_posmap kp, int64_t nk, int64_t a, int64_t b)
     return hi >= lo ? hi - lo + 1 : 0;
 }
 
-// Approximate visible (query, key) pairs of a block pair, from about 256
-// evenly spaced query rows; used only to order the jobs of a launch.
-static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
-    if (nq == 0 || nk == 0) return 0.0;
-    const int64_t step = std::max<int64_t>(1, nq / 256);
-    double sum = 0.0;
+// Visible (query, key) pairs of a block pair, counted on every step-th query
+// row and scaled by step (exact for step = 1).
+static int64_t pair_count(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk,
+                          int64_t step) {
+    if (nq == 0 || nk == 0) return 0;
+    int64_t sum = 0;
     for (int64_t i = 0; i < nq; i += step) {
         const int64_t y = qp.base + qp.stride * i;
         if (m->kind == kCausal) {
-            sum += (double)keys_in_range(kp, nk, 0, y);
+            sum += keys_in_range(kp, nk, 0, y);
             continue;
         }
         // segment of position y: the last run starting at or before y
@@ -281,9 +281,15 @@ static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, 
         int64_t c = keys_in_range(kp, nk, m->segs[sg].run_start, y);
         for (int32_t a = m->segs[sg].parent; a >= 0; a = m->segs[a].parent)
             c += keys_in_range(kp, nk, m->segs[a].run_start, m->segs[a].run_end - 1);
-        sum += (double)c;
+        sum += c;
     }
-    return sum * (double)step;
+    return sum * step;
+}
+
+// Approximate visible pairs from about 256 evenly spaced query rows; orders
+// the jobs of a launch.
+static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
+    return (double)pair_count(m, qp, nq, kp, nk, std::max<int64_t>(1, nq / 256));
 }
 
 // ---------------------------------------------------------------------------
@@ -465,84 +471,141 @@ extern "C" int cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, co
     return run_jobs(jobs, mask, (int)q->n_heads, scale, q->dtype, (int)q->d, st);
 }
 
-extern "C" int cpattn_ring_emulate(int N, const cpattn_tensor* q_blocks, const cpattn_tensor* k_blocks,
-                                   const cpattn_tensor* v_blocks, const cpattn_posmap* pos, const int* ranks,
-                                   int n_ranks_run, const cpattn_mask* mask, float scale, float* const* o_out,
-                                   float* const* lse_out, void* stream) {
-    const char* who = "cpattn_ring_emulate";
+// Ranks that run: all of them (ranks == NULL, n_ranks_run == N) or a list
+// without repeats.
+static int ranks_to_run(int N, const int* ranks, int n_ranks_run, std::vector<int>* run, const char* who) {
+    if (!ranks) {
+        if (n_ranks_run != N) return fail(CPATTN_EINVAL, "%s: ranks is NULL but n_ranks_run != N", who);
+        for (int r = 0; r < N; ++r) run->push_back(r);
+        return CPATTN_OK;
+    }
+    if (n_ranks_run < 0 || n_ranks_run > N) return fail(CPATTN_EINVAL, "%s: n_ranks_run out of range", who);
+    std::vector<char> seen(N, 0);
+    for (int i = 0; i < n_ranks_run; ++i) {
+        if (ranks[i] < 0 || ranks[i] >= N) return fail(CPATTN_EINVAL, "%s: rank %d out of range", who, ranks[i]);
+        if (seen[ranks[i]]) return fail(CPATTN_EINVAL, "%s: rank %d listed twice", who, ranks[i]);
+        seen[ranks[i]] = 1;
+        run->push_back(ranks[i]);
+    }
+    return CPATTN_OK;
+}
+
+// Ring of N ranks that hold C chunks each (chunk i = r * C + c); see
+// cpattn_ring_emulate_chunks in cpattn.h.
+static int ring_core(int N, int C, const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                     const cpattn_posmap* pos, const int* ranks, int n_ranks_run, const cpattn_mask* mask,
+                     float scale, float* const* o_out, float* const* lse_out, void* stream, const char* who) {
     int rc;
     if (N < 1 || N > 64) return fail(CPATTN_EINVAL, "%s: N = %d out of range [1, 64]", who, N);
-    if (!q_blocks || !k_blocks || !v_blocks || !pos || !o_out || !lse_out)
-        return fail(CPATTN_EINVAL, "%s: NULL array argument", who);
+    if (C < 1 || C > 8) return fail(CPATTN_EINVAL, "%s: chunks per rank = %d out of range [1, 8]", who, C);
+    if (!q || !k || !v || !pos || !o_out || !lse_out) return fail(CPATTN_EINVAL, "%s: NULL array argument", who);
     if (!mask) return fail(CPATTN_EINVAL, "%s: mask is NULL", who);
     if ((rc = check_scale(scale, who))) return rc;
     std::vector<int> run;
-    if (!ranks) {
-        if (n_ranks_run != N) return fail(CPATTN_EINVAL, "%s: ranks is NULL but n_ranks_run != N", who);
-        for (int r = 0; r < N; ++r) run.push_back(r);
-    } else {
-        if (n_ranks_run < 0 || n_ranks_run > N) return fail(CPATTN_EINVAL, "%s: n_ranks_run out of range", who);
-        std::vector<char> seen(N, 0);
-        for (int i = 0; i < n_ranks_run; ++i) {
-            if (ranks[i] < 0 || ranks[i] >= N) return fail(CPATTN_EINVAL, "%s: rank %d out of range", who, ranks[i]);
-            if (seen[ranks[i]]) return fail(CPATTN_EINVAL, "%s: rank %d listed twice", who, ranks[i]);
-            seen[ranks[i]] = 1;
-            run.push_back(ranks[i]);
-        }
-    }
-    // every rank's K/V block is visited; only the ranks that run need queries
-    const cpattn_tensor& ref = k_blocks[0];
-    for (int r = 0; r < N; ++r) {
-        if ((rc = check_qkv(&k_blocks[r], &k_blocks[r], &v_blocks[r], who))) return rc;
-        if (k_blocks[r].dtype != ref.dtype || k_blocks[r].d != ref.d || k_blocks[r].n_heads != ref.n_heads)
+    if ((rc = ranks_to_run(N, ranks, n_ranks_run, &run, who))) return rc;
+    const int NC = N * C;
+    // every chunk's K/V is visited; only the chunks of ranks that run need queries
+    const cpattn_tensor& ref = k[0];
+    for (int i = 0; i < NC; ++i) {
+        if ((rc = check_qkv(&k[i], &k[i], &v[i], who))) return rc;
+        if (k[i].dtype != ref.dtype || k[i].d != ref.d || k[i].n_heads != ref.n_heads)
             return fail(CPATTN_EUNSUPPORTED, "%s: every block must share dtype, head dim and heads", who);
-        if ((rc = check_posmap(pos[r], k_blocks[r].n_tok, mask, who, "pos"))) return rc;
+        if ((rc = check_posmap(pos[i], k[i].n_tok, mask, who, "pos"))) return rc;
     }
-    for (int r : run) {
-        if ((rc = check_qkv(&q_blocks[r], &k_blocks[r], &v_blocks[r], who))) return rc;
-        if (q_blocks[r].n_tok != k_blocks[r].n_tok)
-            return fail(CPATTN_EINVAL, "%s: rank %d holds %lld queries but %lld keys at the same positions", who, r,
-                        (long long)q_blocks[r].n_tok, (long long)k_blocks[r].n_tok);
-        if (q_blocks[r].n_tok > 0 && (rc = check_out(o_out[r], lse_out[r], who))) return rc;
-    }
+    for (int r : run)
+        for (int c = 0; c < C; ++c) {
+            const int i = r * C + c;
+            if ((rc = check_qkv(&q[i], &k[i], &v[i], who))) return rc;
+            if (q[i].n_tok != k[i].n_tok)
+                return fail(CPATTN_EINVAL, "%s: chunk %d holds %lld queries but %lld keys at the same positions", who, i,
+                            (long long)q[i].n_tok, (long long)k[i].n_tok);
+            if (q[i].n_tok > 0 && (rc = check_out(o_out[i], lse_out[i], who))) return rc;
+        }
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int heads = (int)ref.n_heads;
     const int dtype = ref.dtype;
     const int d = (int)ref.d;
-    // Each rank's rounds in ring order (block (r - k) mod N in round k),
-    // without the empty ones.  Launch l runs the l-th non-empty round of every
-    // rank: the ranks are independent, and each rank's rounds still merge in
-    // ring order, so this is the ring's result with fewer, fuller launches.
-    std::vector<std::vector<int>> visits(N);
+    // Each query chunk's visits in ring order: in round k the key chunks of
+    // rank (r - k) mod N, in chunk order, without the empty ones.  Launch l
+    // runs the l-th visit of every query chunk: the chunks' outputs are
+    // independent, and each chunk's partials still merge in ring order, so
+    // this is the ring's result with fewer, fuller launches.
+    std::vector<int> units;
+    std::vector<std::vector<int>> visits(NC);
     size_t n_launch = 0;
-    for (int r : run) {
-        for (int k = 0; k < N; ++k) {
-            const int b = ((r - k) % N + N) % N;
-            if (pair_nonempty(mask, pos[r], q_blocks[r].n_tok, pos[b], k_blocks[b].n_tok)) visits[r].push_back(b);
+    for (int r : run)
+        for (int c = 0; c < C; ++c) {
+            const int i = r * C + c;
+            units.push_back(i);
+            for (int kk = 0; kk < N; ++kk) {
+                const int b = ((r - kk) % N + N) % N;
+                for (int c2 = 0; c2 < C; ++c2) {
+                    const int j = b * C + c2;
+                    if (pair_nonempty(mask, pos[i], q[i].n_tok, pos[j], k[j].n_tok)) visits[i].push_back(j);
+                }
+            }
+            n_launch = std::max(n_launch, visits[i].size());
         }
-        n_launch = std::max(n_launch, visits[r].size());
-    }
     for (size_t l = 0; l < n_launch; ++l) {
         std::vector<JobArgs> jobs;
         std::vector<double> work;
-        for (int r : run) {
-            if (l >= visits[r].size()) continue;
-            const int b = visits[r][l];
-            jobs.push_back(make_job(&q_blocks[r], &k_blocks[b], &v_blocks[b], pos[r], pos[b], o_out[r], lse_out[r],
-                                    l > 0 ? 1 : 0));
-            work.push_back(pair_estimate(mask, pos[r], q_blocks[r].n_tok, pos[b], k_blocks[b].n_tok));
+        for (int i : units) {
+            if (l >= visits[i].size()) continue;
+            const int j = visits[i][l];
+            jobs.push_back(make_job(&q[i], &k[j], &v[j], pos[i], pos[j], o_out[i], lse_out[i], l > 0 ? 1 : 0));
+            work.push_back(pair_estimate(mask, pos[i], q[i].n_tok, pos[j], k[j].n_tok));
         }
         // heaviest job first: the launch's last workgroups are its lightest
         std::vector<size_t> idx(jobs.size());
-        for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+        for (size_t x = 0; x < idx.size(); ++x) idx[x] = x;
         std::stable_sort(idx.begin(), idx.end(), [&](size_t x, size_t y) { return work[x] > work[y]; });
         std::vector<JobArgs> sorted;
-        for (size_t i : idx) sorted.push_back(jobs[i]);
+        for (size_t x : idx) sorted.push_back(jobs[x]);
         if ((rc = run_jobs(sorted, mask, heads, scale, dtype, d, st))) return rc;
     }
-    for (int r : run)
-        if (visits[r].empty() && (rc = launch_fill(o_out[r], lse_out[r], heads * q_blocks[r].n_tok, d, st))) return rc;
+    for (int i : units)
+        if (visits[i].empty() && (rc = launch_fill(o_out[i], lse_out[i], heads * q[i].n_tok, d, st))) return rc;
+    return CPATTN_OK;
+}
+
+extern "C" int cpattn_ring_emulate(int N, const cpattn_tensor* q_blocks, const cpattn_tensor* k_blocks,
+                                   const cpattn_tensor* v_blocks, const cpattn_posmap* pos, const int* ranks,
+                                   int n_ranks_run, const cpattn_mask* mask, float scale, float* const* o_out,
+                                   float* const* lse_out, void* stream) {
+    return ring_core(N, 1, q_blocks, k_blocks, v_blocks, pos, ranks, n_ranks_run, mask, scale, o_out, lse_out, stream,
+                     "cpattn_ring_emulate");
+}
+
+extern "C" int cpattn_ring_emulate_chunks(int N, int C, const cpattn_tensor* q_chunks, const cpattn_tensor* k_chunks,
+                                          const cpattn_tensor* v_chunks, const cpattn_posmap* pos, const int* ranks,
+                                          int n_ranks_run, const cpattn_mask* mask, float scale,
+                                          float* const* o_out, float* const* lse_out, void* stream) {
+    return ring_core(N, C, q_chunks, k_chunks, v_chunks, pos, ranks, n_ranks_run, mask, scale, o_out, lse_out,
+                     stream, "cpattn_ring_emulate_chunks");
+}
+
+extern "C" int cpattn_ring_plan(int N, int C, const int64_t* n_tok, const cpattn_posmap* pos,
+                                const cpattn_mask* mask, int64_t* work) {
+    const char* who = "cpattn_ring_plan";
+    int rc;
+    if (N < 1 || N > 64) return fail(CPATTN_EINVAL, "%s: N = %d out of range [1, 64]", who, N);
+    if (C < 1 || C > 8) return fail(CPATTN_EINVAL, "%s: chunks per rank = %d out of range [1, 8]", who, C);
+    if (!n_tok || !pos || !work) return fail(CPATTN_EINVAL, "%s: NULL array argument", who);
+    if (!mask) return fail(CPATTN_EINVAL, "%s: mask is NULL", who);
+    for (int i = 0; i < N * C; ++i) {
+        if (n_tok[i] < 0 || n_tok[i] > INT32_MAX) return fail(CPATTN_EINVAL, "%s: chunk %d size out of range", who, i);
+        if ((rc = check_posmap(pos[i], n_tok[i], mask, who, "pos"))) return rc;
+    }
+    for (int r = 0; r < N; ++r)
+        for (int kk = 0; kk < N; ++kk) {
+            const int b = ((r - kk) % N + N) % N;
+            int64_t w = 0;
+            for (int c = 0; c < C; ++c)
+                for (int c2 = 0; c2 < C; ++c2)
+                    w += pair_count(mask, pos[r * C + c], n_tok[r * C + c], pos[b * C + c2], n_tok[b * C + c2], 1);
+            work[r * N + kk] = w;
+        }
     return CPATTN_OK;
 }
 

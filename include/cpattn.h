@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 1
+#define CPATTN_VERSION_MINOR 2
 
 typedef enum {
     CPATTN_OK = 0,
@@ -159,6 +159,38 @@ int cpattn_ring_emulate(int N, const cpattn_tensor* q_blocks, const cpattn_tenso
                         const cpattn_tensor* v_blocks, const cpattn_posmap* pos,
                         const int* ranks, int n_ranks_run, const cpattn_mask* mask, float scale,
                         float* const* o_out, float* const* lse_out, void* stream);
+
+/* Ring emulation where each rank holds C chunks of the sequence, for
+ * layouts that are not one affine run per rank.  The zig-zag (folded) layout
+ * of the causal load-balancing section of the ML-systems lesson splits the
+ * sequence into 2N chunks and gives rank r chunks r and 2N-1-r (C = 2), so
+ * that every rank does the same causal work (the lesson's worked example (c):
+ * 9 pairs per rank instead of 3, 7, 11, 15).
+ *   Arrays of N*C entries, chunk c of rank r at index r*C + c: q_chunks,
+ *   k_chunks, v_chunks (tensors as in cpattn_ring_emulate; a chunk's queries
+ *   and keys sit at the same positions pos[r*C + c]) and o_out, lse_out
+ *   (device pointers, [H][n_tok][d] and [H][n_tok] fp32 per chunk; entries of
+ *   ranks not run may be NULL).
+ * In round k every chunk of rank r meets every key chunk of rank (r - k) mod N
+ * (in chunk order); pairs with no visible key are skipped; the partials of a
+ * query chunk merge in that order.  C = 1 is cpattn_ring_emulate.
+ * 1 <= N <= 64, 1 <= C <= 8.  Errors as for cpattn_ring_emulate. */
+int cpattn_ring_emulate_chunks(int N, int C, const cpattn_tensor* q_chunks, const cpattn_tensor* k_chunks,
+                               const cpattn_tensor* v_chunks, const cpattn_posmap* pos,
+                               const int* ranks, int n_ranks_run, const cpattn_mask* mask, float scale,
+                               float* const* o_out, float* const* lse_out, void* stream);
+
+/* Per-rank work report of a ring (host only; no device work).  For N ranks
+ * with C chunks each (chunk r*C + c has n_tok[r*C + c] tokens at positions
+ * pos[r*C + c]), work[r*N + k] receives the number of visible (query, key)
+ * pairs, per head, of rank r's queries against the keys held by rank
+ * (r - k) mod N, i.e. rank r's work in round k (ML-systems lesson, causal
+ * load balancing: a ring round lasts as long as its busiest rank).  Counted
+ * exactly from the mask with integer arithmetic.  n_tok, pos and work are
+ * host arrays (N*C, N*C and N*N entries).  EINVAL on bad sizes or positions
+ * outside the mask. */
+int cpattn_ring_plan(int N, int C, const int64_t* n_tok, const cpattn_posmap* pos, const cpattn_mask* mask,
+                     int64_t* work);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* cpattn_last_error(void);
