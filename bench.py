@@ -121,6 +121,54 @@ def block_pair_counts(seg: np.ndarray, parent: np.ndarray, c: int, N: int) -> np
     return out
 
 
+def load_balance(cp, workloads, torch, dev, reps: int = 2):
+    """Causal ring of 8 ranks over 32768 tokens (32 heads, d 128, bf16),
+    contiguous blocks vs the zig-zag layout: every (rank, round) partial timed
+    on its own with HIP events (all its chunk pairs), the ring time being the
+    sum over rounds of the slowest rank (ranks of a real ring wait for each
+    other every round).  Work per (rank, round) from cpattn_ring_plan."""
+    H, n, d, N = 32, 32768, 128, 8
+    q, k, v = workloads.qkv(1, H, n, d, "bf16")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    mask = cp.Mask.causal(n)
+    out = {}
+    for name, C in (("contiguous", 1), ("zigzag", 2)):
+        c = n // (N * C)
+        chunks = list(range(N)) if C == 1 else [ch for r in range(N) for ch in (r, 2 * N - 1 - r)]
+        view = lambda t, ch: t[:, ch * c:(ch + 1) * c]
+        work = cp.ring_plan([c] * (N * C), [(ch * c, 1) for ch in chunks], mask, chunks_per_rank=C)
+        o = torch.empty((H, c, d), dtype=torch.float32, device=dev)
+        l = torch.empty((H, c), dtype=torch.float32, device=dev)
+        t = np.zeros((N, N))
+        stream = torch.cuda.current_stream()
+        for r in range(N):
+            for kk in range(N):
+                b = (r - kk) % N
+                pairs = [(qi, kj) for qi in chunks[r * C:(r + 1) * C] for kj in chunks[b * C:(b + 1) * C]]
+                def rank_round():
+                    for qi, kj in pairs:
+                        cp.partial(view(qd, qi), view(kd, kj), view(vd, kj), mask, (qi * c, 1), (kj * c, 1),
+                                   out=(o, l), stream=stream)
+                rank_round()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    rank_round()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t[r, kk] = e0.elapsed_time(e1) / reps
+        out[name] = {"per_rank_ms": [round(float(x), 3) for x in t.sum(axis=1)],
+                     "per_rank_pairs": [int(x) for x in work.sum(axis=1)],
+                     "ring_ms": round(float(t.max(axis=0).sum()), 3),
+                     "ring_pairs": int(work.max(axis=0).sum())}
+    mask.free()
+    out["workload"] = "causal ring, 32 heads x 32768 tokens, d 128, bf16, N = 8: contiguous blocks of 4096 vs " \
+                      "zig-zag chunks of 2048 (rank r: chunks r and 15 - r); ring time = sum over rounds of the " \
+                      "slowest rank's partial"
+    out["ring_speedup"] = round(out["contiguous"]["ring_ms"] / out["zigzag"]["ring_ms"], 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +178,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample: query rows per head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing (diagnostic runs)")
+    ap.add_argument("--no-balance", action="store_true", help="skip the contiguous vs zig-zag ring comparison")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="calibration run: only time a plain device copy of this many MiB")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -278,6 +327,9 @@ def main():
                   "bytes": merge_bytes, "GB/s": round(merge_gbs, 1),
                   "frac_of_hbm_peak": round(merge_gbs / PEAK_HBM_GBS, 4)},
     }
+
+    if not args.no_balance:
+        result["load_balance"] = load_balance(cp, workloads, torch, dev)
 
     if not args.no_cpu:
         import oracle
