@@ -169,6 +169,38 @@ def load_balance(cp, workloads, torch, dev, reps: int = 2):
     return out
 
 
+def gqa_ring(cp, workloads, torch, dev, seg, parent, N, flops, steps: int = 10):
+    """The same tree row and ring with grouped-query attention: 32 query heads
+    over 4 K/V heads (the pages' measured shape).  Same visible FLOPs; 8x less
+    K/V data."""
+    H, hkv, d = 32, 4, 128
+    n = len(seg)
+    c = n // N
+    q, _, _ = workloads.qkv(0, H, n, d, "bf16")
+    _, k, v = workloads.qkv(1, hkv, n, d, "bf16")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    Q, K, V = blk(qd), blk(kd), blk(vd)
+    pos = [(r * c, 1) for r in range(N)]
+    mask = cp.Mask.tree(seg, parent)
+    outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
+                torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    mask.free()
+    return {"workload": "tree64k ring of %d, 32 query heads over 4 K/V heads, d 128, bf16" % N,
+            "ms_per_step": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +362,7 @@ def main():
 
     if not args.no_balance:
         result["load_balance"] = load_balance(cp, workloads, torch, dev)
+        result["gqa"] = gqa_ring(cp, workloads, torch, dev, seg, parent, N, flops)
 
     if not args.no_cpu:
         import oracle

@@ -179,7 +179,8 @@ def partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, q_pos
             scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
             accumulate: bool = False, stream=None):
     """(O [H, n_q, d] fp32, LSE [H, n_q] fp32) of ``q`` against the block
-    ``k``/``v``.  Positions: row i of the query block sits at
+    ``k``/``v`` (which may have H / g heads: grouped-query attention, query
+    head h reads K/V head h // g).  Positions: row i of the query block sits at
     ``q_pos[0] + q_pos[1] * i`` (likewise ``k_pos``).  With ``accumulate``
     the result is merged into ``out`` (which must hold a running result)."""
     H, nq, d = q.shape
@@ -236,7 +237,7 @@ def ring_emulate(q_blocks: Sequence[Optional[torch.Tensor]], k_blocks: Sequence[
         raise ValueError("every rank needs a q/k/v block and positions")
     run = list(range(N)) if ranks is None else [int(r) for r in ranks]
     d = k_blocks[0].shape[2]
-    H = k_blocks[0].shape[0]
+    H = q_blocks[run[0]].shape[0] if run else k_blocks[0].shape[0]   # query heads (K/V may have fewer)
     if outs is None:
         outs = {}
         for r in run:
@@ -282,7 +283,7 @@ def ring_emulate_chunks(q_chunks: Sequence[Optional[torch.Tensor]], k_chunks: Se
     run = list(range(N)) if ranks is None else [int(r) for r in ranks]
     units = [r * C + c for r in run for c in range(C)]
     d = k_chunks[0].shape[2]
-    H = k_chunks[0].shape[0]
+    H = q_chunks[units[0]].shape[0] if units else k_chunks[0].shape[0]   # query heads (K/V may have fewer)
     if outs is None:
         outs = {}
         for i in units:

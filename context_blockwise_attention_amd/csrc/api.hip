@@ -383,6 +383,7 @@ static JobArgs make_job(const cpattn_tensor* q, const cpattn_tensor* k, const cp
     j.accumulate = accumulate;
     const int bm = rows_per_wg(q->dtype);
     j.q_tiles = (int32_t)((q->n_tok + bm - 1) / bm);
+    j.kv_group = (int32_t)(q->n_heads / k->n_heads);
     return j;
 }
 
@@ -429,9 +430,10 @@ static int check_qkv(const cpattn_tensor* q, const cpattn_tensor* k, const cpatt
     if (q->dtype != k->dtype || q->dtype != v->dtype)
         return fail(CPATTN_EUNSUPPORTED, "%s: q, k and v must share one dtype", who);
     if (q->d != k->d || q->d != v->d) return fail(CPATTN_EUNSUPPORTED, "%s: q, k and v must share one head dim", who);
-    if (q->n_heads != k->n_heads || q->n_heads != v->n_heads)
-        return fail(CPATTN_EINVAL, "%s: head counts differ (q %lld, k %lld, v %lld)", who, (long long)q->n_heads,
-                    (long long)k->n_heads, (long long)v->n_heads);
+    // grouped-query attention: every K/V head serves the same number of query heads
+    if (k->n_heads != v->n_heads || q->n_heads % k->n_heads != 0)
+        return fail(CPATTN_EINVAL, "%s: head counts (q %lld, k %lld, v %lld): k and v must match and divide q", who,
+                    (long long)q->n_heads, (long long)k->n_heads, (long long)v->n_heads);
     if (k->n_tok != v->n_tok) return fail(CPATTN_EINVAL, "%s: k and v token counts differ", who);
     return CPATTN_OK;
 }
@@ -523,7 +525,12 @@ static int ring_core(int N, int C, const cpattn_tensor* q, const cpattn_tensor* 
         }
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const int heads = (int)ref.n_heads;
+    if (run.empty()) return CPATTN_OK;
+    const int heads = (int)q[run[0] * C].n_heads;   // query heads (K/V may have fewer: grouped-query attention)
+    for (int r : run)
+        for (int c = 0; c < C; ++c)
+            if (q[r * C + c].n_heads != heads)
+                return fail(CPATTN_EINVAL, "%s: every query chunk must have the same head count", who);
     const int dtype = ref.dtype;
     const int d = (int)ref.d;
     // Each query chunk's visits in ring order: in round k the key chunks of

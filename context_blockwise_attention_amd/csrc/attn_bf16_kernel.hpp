@@ -178,8 +178,9 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     const int jlim = min(J.n_k - 1, ypos < J.kbase ? -1 : (ypos - J.kbase) / J.kstride);
 
     const __bf16* qh = reinterpret_cast<const __bf16*>(J.q) + head * J.q_sh;
-    const __bf16* kh = reinterpret_cast<const __bf16*>(J.k) + head * J.k_sh;
-    const __bf16* vh = reinterpret_cast<const __bf16*>(J.v) + head * J.v_sh;
+    const int kv_head = head / J.kv_group;   // grouped-query attention: query heads share a K/V head
+    const __bf16* kh = reinterpret_cast<const __bf16*>(J.k) + kv_head * J.k_sh;
+    const __bf16* vh = reinterpret_cast<const __bf16*>(J.v) + kv_head * J.v_sh;
 
     bf16x8 qreg[TT::DSTEPS];
     {

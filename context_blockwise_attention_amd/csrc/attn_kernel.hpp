@@ -63,6 +63,7 @@ struct JobArgs {
     int32_t n_q, n_k;
     int32_t accumulate;
     int32_t q_tiles;   // ceil(n_q / rows per workgroup)
+    int32_t kv_group;  // query heads per key/value head (grouped-query attention; 1 = one K/V head per query head)
 };
 
 struct MaskArgs {
@@ -87,7 +88,8 @@ struct LaunchArgs {
 // ---------------------------------------------------------------------------
 // Work slot of workgroup `bid` -> (job, head, q-tile), or false for an empty
 // slot.  Workgroups are dispatched round-robin over the 8 XCDs (bid % 8).
-// With at least 8 heads, XCD x runs the heads h with h % 8 == x of every job:
+// With at least 8 heads, XCD x runs one eighth of the heads of every job
+// (contiguous ranges when the head count divides by 8, else h = x mod 8):
 // every XCD gets the same share of every job, so no XCD is left with only the
 // light job of a launch.  Within an XCD the items run one (job, head) group
 // after another, the group's q-tiles heaviest (last) first, so the ~32
@@ -99,13 +101,18 @@ __device__ __forceinline__ bool work_item(const LaunchArgs& a, int bid, int* job
     const int x = bid & 7;
     int p = by_xcd ? (bid >> 3) : bid;
     const int hg = by_xcd ? a.heads_per_xcd : a.heads;   // head groups per job seen by this slot stream
+    // heads divisible by 8: XCD x runs the contiguous heads [x*hg, (x+1)*hg),
+    // so the query heads of one K/V head (grouped-query attention) share as
+    // few L2s as possible; otherwise heads h = x (mod 8), which balances the
+    // XCDs when the count is uneven
+    const bool ranges = by_xcd && (a.heads & 7) == 0;
     for (int j = 0; j < a.n_jobs; ++j) {
         const int qt = a.jobs[j].q_tiles;
         const int n = hg * qt;
         if (p < n) {
             const int hi = p / qt;
             const int r = p - hi * qt;
-            const int h = by_xcd ? x + 8 * hi : hi;
+            const int h = !by_xcd ? hi : ranges ? x * hg + hi : x + 8 * hi;
             if (h >= a.heads) return false;
             *job = j;
             *head = h;
@@ -407,8 +414,9 @@ partial_attention_kernel(const LaunchArgs args) {
     const int ypos = J.qbase + J.qstride * qi;
 
     const T* qh = reinterpret_cast<const T*>(J.q) + head * J.q_sh;
-    const T* kh = reinterpret_cast<const T*>(J.k) + head * J.k_sh;
-    const T* vh = reinterpret_cast<const T*>(J.v) + head * J.v_sh;
+    const int kv_head = head / J.kv_group;
+    const T* kh = reinterpret_cast<const T*>(J.k) + kv_head * J.k_sh;
+    const T* vh = reinterpret_cast<const T*>(J.v) + kv_head * J.v_sh;
     const auto qr = make_rsrc(qh, ((J.n_q - 1) * J.q_st + D) * (int)sizeof(T));
     const auto kr = make_rsrc(kh, ((J.n_k - 1) * J.k_st + D) * (int)sizeof(T));
     const auto vr = make_rsrc(vh, ((J.n_k - 1) * J.v_st + D) * (int)sizeof(T));

@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 2
+#define CPATTN_VERSION_MINOR 3
 
 typedef enum {
     CPATTN_OK = 0,
@@ -117,7 +117,10 @@ int64_t cpattn_mask_npos(const cpattn_mask* m);
 /* Partial attention of one query block against one key/value block: the
  * (O, LSE) pair of one ring round ("Context Parallelism in ART", sections 02
  * and 03; the masks are those of section 02).
- *   q: [H][n_q][d], k and v: [H][n_k][d]; one dtype, one d, one H.
+ *   q: [H][n_q][d], k and v: [H_kv][n_k][d]; one dtype, one d.  H_kv must
+ *      divide H: grouped-query attention ("Context Parallelism in ART",
+ *      section 02, the measured model has 32 query and 4 KV heads), query
+ *      head h reads K/V head h / (H / H_kv); H_kv = H is plain multi-head.
  *   q_pos, k_pos: global positions of the rows (checked against the mask's
  *                 n_pos: every row's position must lie in [0, n_pos)).
  *   scale: multiplies q.k before the softmax (usually 1/sqrt(d)).
@@ -140,7 +143,8 @@ int cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_
 int cpattn_merge(int n_parts, const float* const* o_parts, const float* const* lse_parts,
                  int64_t n_rows, int64_t d, float* o_out, float* lse_out, void* stream);
 
-/* Ring emulation on one GPU.  N ranks each hold one query block q_blocks[r]
+/* Ring emulation on one GPU (K/V blocks may have fewer heads than the
+ * queries, as in cpattn_partial).  N ranks each hold one query block q_blocks[r]
  * and one key/value block (k_blocks[r], v_blocks[r]) with positions pos[r].
  * For each rank r in ranks[0..n_ranks_run), every round k = 0..N-1 computes
  * the partial of q_blocks[r] against the K/V block of rank (r - k) mod N and

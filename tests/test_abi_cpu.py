@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_error_string(L):
     import context_blockwise_attention_amd as cp
-    assert cp.version() == (0, 2)
+    assert cp.version() == (0, 3)
     assert isinstance(L.cpattn_last_error(), bytes)
 
 
@@ -90,6 +90,8 @@ def test_partial_validation(L):
     assert _partial(L, cp, _tensor(cp, d=96), t, t, h) == EUNSUPPORTED             # head dim
     assert _partial(L, cp, t, _tensor(cp, dtype=1), t, h) == EUNSUPPORTED          # mixed dtypes
     assert _partial(L, cp, t, _tensor(cp, H=3), t, h) == EINVAL                    # head counts differ
+    assert _partial(L, cp, t, _tensor(cp, H=1), t, h) == EINVAL                    # k and v heads differ
+    assert _partial(L, cp, t, _tensor(cp, H=4), _tensor(cp, H=4), h) == EINVAL     # K/V heads do not divide q heads
     assert _partial(L, cp, t, t, _tensor(cp, n=15), h) == EINVAL                   # k/v lengths differ
     assert _partial(L, cp, _tensor(cp, data=0x1008), t, t, h) == EUNSUPPORTED      # alignment
     assert _partial(L, cp, _tensor(cp, st=132), t, t, h) == EUNSUPPORTED           # stride not x8
