@@ -75,6 +75,8 @@ def _load():
                                          ctypes.c_double, p, i64, p, p, ctypes.c_int]
         lib.oracle_merge2.restype = None
         lib.oracle_merge2.argtypes = [i64, i64, p, p, p, p]
+        lib.oracle_apply_sink.restype = None
+        lib.oracle_apply_sink.argtypes = [i64, i64, i64, p, p, p]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -213,6 +215,21 @@ def merge(parts):
     for p in parts[1:]:
         acc = merge2(acc, p)
     return acc
+
+
+def apply_sink(O, L, a):
+    """Learned sink logits ``a`` [H] applied once to a complete result
+    ``(O [H, n, d], L [H, n])`` ("Context Parallelism in ART", section 06):
+    ``L_total = logaddexp(L, a)``, ``O * exp(L - L_total)``.  Returns new
+    fp64 arrays."""
+    lib = _load()
+    Oc = np.array(O, dtype=np.float64, copy=True, order="C")
+    Lc = np.array(L, dtype=np.float64, copy=True, order="C")
+    ac = np.ascontiguousarray(a, dtype=np.float64)
+    if Oc.ndim != 3 or Lc.shape != Oc.shape[:2] or ac.shape != (Oc.shape[0],):
+        raise ValueError("apply_sink expects O [H, n, d], L [H, n], a [H]")
+    lib.oracle_apply_sink(Oc.shape[0], Oc.shape[1], Oc.shape[2], Oc.ctypes.data, Lc.ctypes.data, ac.ctypes.data)
+    return Oc, Lc
 
 
 def ring(Q_r, q_pos, K_blocks, V_blocks, kv_pos, rank: int, mask=Causal(), scale=None,

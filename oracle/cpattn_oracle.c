@@ -27,6 +27,9 @@
  *    with m read as max(L_A, L_B).  An n-way merge is a left fold of the
  *    two-way merge, which the page states is composable.
  *
+ *  - The learned attention sink, applied once to a complete result (same
+ *    page, section 06): oracle_apply_sink.
+ *
  *  Readings where the pages are silent (each is also listed in the design doc):
  *  a query with no visible key gives O = 0 and L = -inf; merging with such a
  *  partial leaves the other side unchanged; merging two empty partials gives
@@ -201,6 +204,29 @@ void oracle_merge(int n_parts, const double* const* O_parts, const double* const
     memcpy(O, O_parts[0], sizeof(double) * (size_t)(n_rows * dv));
     memcpy(L, L_parts[0], sizeof(double) * (size_t)n_rows);
     for (int p = 1; p < n_parts; ++p) oracle_merge2(n_rows, dv, O, L, O_parts[p], L_parts[p]);
+}
+
+/*
+ * oracle_apply_sink: a learned attention-sink logit a_h per head adds
+ * probability mass with zero value to the softmax denominator, once per query
+ * ("Context Parallelism in ART", section 06, the sink as probability mass:
+ * L_total = logaddexp(L, a), w = exp(L - L_total), y = w o).  O is
+ * [n_heads][n_rows][dv], L is [n_heads][n_rows], a is [n_heads]; in place.
+ * logaddexp is taken in its max-shifted form.  A row with no visible key
+ * (L = -inf) gets w = 0 and L_total = a (all of its mass is the sink's).
+ */
+void oracle_apply_sink(int64_t n_heads, int64_t n_rows, int64_t dv, double* O, double* L, const double* a) {
+    for (int64_t h = 0; h < n_heads; ++h) {
+        for (int64_t r = 0; r < n_rows; ++r) {
+            double l = L[h * n_rows + r];
+            double m = l > a[h] ? l : a[h];
+            double lt = (m == -INFINITY) ? -INFINITY : m + log(exp(l - m) + exp(a[h] - m));
+            double w = (l == -INFINITY) ? 0.0 : exp(l - lt);
+            double* o = O + (h * n_rows + r) * dv;
+            for (int64_t c = 0; c < dv; ++c) o[c] = w * o[c];
+            L[h * n_rows + r] = lt;
+        }
+    }
 }
 
 int oracle_max_threads(void) {

@@ -23,6 +23,9 @@ MUTANTS = {
                             "widen(V, dtype, h * v_sh + j * v_st + c)"),
     "scale_dropped": ("s[a] = acc * scale;", "s[a] = acc;"),
     "output_unnormalised": ("double p = exp(s[a] - lse);", "double p = exp(s[a] - m);"),
+    "sink_weight_inverted": ("double w = (l == -INFINITY) ? 0.0 : exp(l - lt);",
+                             "double w = (l == -INFINITY) ? 0.0 : exp(lt - l);"),
+    "sink_mass_dropped": ("m + log(exp(l - m) + exp(a[h] - m));", "m + log(exp(l - m));"),
 }
 
 
