@@ -396,6 +396,25 @@ def main():
         result["parity_sample"] = {"rows": rows_per_head * H, "max_abs_dO": worst_o, "max_abs_dLSE": worst_l,
                                    "tol_O": 2e-2, "tol_LSE": 1e-3,
                                    "ok": bool(worst_o <= 2e-2 and worst_l <= 1e-3)}
+    # learned sink applied once to the complete result (HBM-bound: reads and
+    # writes every row's d + 1 floats), on copies of the ranks' outputs
+    so = torch.cat([outs[r][0] for r in range(N)], 1).contiguous()
+    sl = torch.cat([outs[r][1] for r in range(N)], 1).contiguous()
+    sink = torch.zeros((H,), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        cp.apply_sink(so, sl, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        cp.apply_sink(so, sl, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sink_ms = e0.elapsed_time(e1) / reps
+    sink_bytes = 2 * H * n * (d + 1) * 4
+    result["sink"] = {"kernel": "sink_kernel", "rows": H * n, "d": d, "ms": round(sink_ms, 4), "bytes": sink_bytes,
+                      "GB/s": round(sink_bytes / (sink_ms * 1e-3) / 1e9, 1),
+                      "frac_of_hbm_peak": round(sink_bytes / (sink_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     mask.free()
     print(json.dumps(result), flush=True)
 

@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
 * :func:`ring_emulate_chunks` -- the same for ranks that hold several chunks
   (the zig-zag layout).
 * :func:`ring_plan` -- per-rank, per-round visible-pair counts (host only).
+* :func:`apply_sink` -- learned attention-sink logits applied once to a
+  complete result.
 """
 from __future__ import annotations
 
@@ -77,8 +79,10 @@ def lib():
         L.cpattn_ring_emulate_chunks.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int, P,
                                                  ctypes.c_float, P, P, P]
         L.cpattn_ring_plan.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P]
+        L.cpattn_apply_sink.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
         for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
-                  "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan"):
+                  "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan",
+                  "cpattn_apply_sink"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -325,3 +329,18 @@ def ring_plan(n_tok: Sequence[int], pos: Sequence[Tuple[int, int]], mask: Mask, 
     work = np.zeros(N * N, dtype=np.int64)
     _check(lib().cpattn_ring_plan(N, C, nt, pd, mask.handle, work.ctypes.data))
     return work.reshape(N, N)
+
+
+def apply_sink(o: torch.Tensor, lse: torch.Tensor, sink_logits: torch.Tensor, stream=None):
+    """Applies per-head sink logits ``sink_logits`` [H] (fp32, natural log)
+    once to a complete result ``(o [H, n, d], lse [H, n])``, in place:
+    ``lse <- logaddexp(lse, a)``, ``o <- o * exp(lse_old - lse)``."""
+    H, n, d = o.shape
+    if lse.shape != (H, n) or sink_logits.shape != (H,):
+        raise ValueError("apply_sink expects o [H, n, d], lse [H, n], sink_logits [H]")
+    for t, name in ((o, "o"), (lse, "lse"), (sink_logits, "sink_logits")):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous fp32 device tensor" % name)
+    _check(lib().cpattn_apply_sink(o.data_ptr(), lse.data_ptr(), sink_logits.data_ptr(), H, n, d,
+                                   _stream(stream)))
+    return o, lse

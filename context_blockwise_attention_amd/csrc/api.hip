@@ -651,3 +651,31 @@ extern "C" int cpattn_merge(int n_parts, const float* const* o_parts, const floa
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? CPATTN_OK : hip_fail(e, "merge launch");
 }
+
+extern "C" int cpattn_apply_sink(float* o, float* lse, const float* sink_logits, int64_t n_heads, int64_t n_rows,
+                                 int64_t d, void* stream) {
+    const char* who = "cpattn_apply_sink";
+    if (n_heads < 1 || n_rows < 0 || d < 4 || d > (1 << 20)) return fail(CPATTN_EINVAL, "%s: bad sizes", who);
+    if (d % 4 != 0) return fail(CPATTN_EUNSUPPORTED, "%s: d must be a multiple of 4", who);
+    if (n_rows == 0) return CPATTN_OK;
+    if (!o || !lse || !sink_logits) return fail(CPATTN_EINVAL, "%s: NULL pointer", who);
+    if ((reinterpret_cast<uintptr_t>(o) & 15) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3) != 0 ||
+        (reinterpret_cast<uintptr_t>(sink_logits) & 3) != 0)
+        return fail(CPATTN_EUNSUPPORTED, "%s: o must be 16-byte aligned, lse and sink_logits 4-byte aligned", who);
+    SinkArgs a{};
+    a.o = o;
+    a.lse = lse;
+    a.sink = sink_logits;
+    a.rows = n_heads * n_rows;
+    a.rows_per_head = n_rows;
+    a.d = (int32_t)d;
+    a.tpr = (int32_t)std::min<int64_t>(256, d / 4);
+    while (256 % a.tpr) --a.tpr;
+    const int64_t rows_per_block = 256 / a.tpr;
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many rows", who);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(sink_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "sink launch");
+}

@@ -86,4 +86,48 @@ __global__ void __launch_bounds__(256) fill_empty_kernel(float* o, float* lse, i
     if (i < rows) lse[i] = -INFINITY;
 }
 
+// Learned attention sink applied once to a complete result ("Context
+// Parallelism in ART", section 06: the sink is probability mass with zero
+// value): L' = logaddexp(L, a_h), O' = O * exp(L - L').  One row of d floats
+// per `tpr` consecutive threads, d % 4 == 0, in place.  A row with no visible
+// key (L = -inf) becomes (0, a_h).  HBM-bound: reads and writes d + 1 floats.
+struct SinkArgs {
+    float* o;
+    float* lse;
+    const float* sink;     // [heads] logits, natural-log units
+    int64_t rows;          // heads * rows per head
+    int64_t rows_per_head;
+    int32_t d;
+    int32_t tpr;
+};
+
+__global__ void __launch_bounds__(256) sink_kernel(const SinkArgs a) {
+    const int rows_per_block = 256 / a.tpr;
+    const int sub = threadIdx.x / a.tpr;
+    const int t = threadIdx.x % a.tpr;
+    const int64_t row = (int64_t)blockIdx.x * rows_per_block + sub;
+    const bool active = sub < rows_per_block && row < a.rows;
+    float l = -INFINITY, lt = -INFINITY, w = 0.f;
+    if (active) {
+        l = a.lse[row];
+        const float s = a.sink[row / a.rows_per_head];
+        const float m = fmaxf(l, s);
+        lt = m == -INFINITY ? -INFINITY : m + logf(expf(l - m) + expf(s - m));
+        w = l == -INFINITY ? 0.f : expf(l - lt);
+    }
+    // a row may span several waves: all of them read its LSE before it is replaced
+    __syncthreads();
+    if (!active) return;
+    float4* o = reinterpret_cast<float4*>(a.o + row * a.d);
+    for (int c = t; c < a.d / 4; c += a.tpr) {
+        float4 v = o[c];
+        v.x *= w;
+        v.y *= w;
+        v.z *= w;
+        v.w *= w;
+        o[c] = v;
+    }
+    if (t == 0) a.lse[row] = lt;
+}
+
 }  // namespace cpattn

@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 3
+#define CPATTN_VERSION_MINOR 4
 
 typedef enum {
     CPATTN_OK = 0,
@@ -195,6 +195,20 @@ int cpattn_ring_emulate_chunks(int N, int C, const cpattn_tensor* q_chunks, cons
  * outside the mask. */
 int cpattn_ring_plan(int N, int C, const int64_t* n_tok, const cpattn_posmap* pos, const cpattn_mask* mask,
                      int64_t* work);
+
+/* Learned attention sink, applied once to a complete (fully merged) result
+ * ("Context Parallelism in ART", section 06: a per-head sink logit adds
+ * probability mass with zero value to the softmax denominator, and belongs to
+ * the whole query, not to every ring stage):
+ *   L' = logaddexp(L, a_h),  O' = O * exp(L - L'),  in place.
+ *   o: [n_heads][n_rows][d] fp32 (16-byte aligned), lse: [n_heads][n_rows]
+ *   fp32, sink_logits: [n_heads] fp32 in natural-log units; all device memory.
+ * A row with no visible key (L = -inf) becomes (0, a_h).  Applying it to each
+ * partial before merging would count the sink once per partial; call it after
+ * the last merge.  EUNSUPPORTED if d % 4 != 0 or misaligned; EINVAL on bad
+ * sizes or NULL pointers. */
+int cpattn_apply_sink(float* o, float* lse, const float* sink_logits, int64_t n_heads, int64_t n_rows,
+                      int64_t d, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* cpattn_last_error(void);
