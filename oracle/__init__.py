@@ -72,7 +72,7 @@ def _load():
         lib.oracle_attention.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                          p, i64, i64, p, i64, i64, p, i64, i64,
                                          p, p, ctypes.c_int, p, i64, p, ctypes.c_int32,
-                                         ctypes.c_double, p, i64, p, p, ctypes.c_int]
+                                         i64, ctypes.c_double, p, i64, p, p, ctypes.c_int]
         lib.oracle_merge2.restype = None
         lib.oracle_merge2.argtypes = [i64, i64, p, p, p, p]
         lib.oracle_apply_sink.restype = None
@@ -91,7 +91,9 @@ def max_threads() -> int:
 # ----------------------------------------------------------------------------
 @dataclass(frozen=True)
 class Causal:
-    """Key visible iff its global position <= the query's."""
+    """Key visible iff its global position <= the query's; with ``window``
+    > 0 also within ``window`` positions of it, the query itself included."""
+    window: int = 0
 
 
 @dataclass(frozen=True)
@@ -102,9 +104,12 @@ class Full:
 @dataclass(frozen=True)
 class Tree:
     """Prefix tree: ``seg[x]`` = segment of global position x, ``parent[s]`` =
-    parent segment of s (-1 for a root)."""
+    parent segment of s (-1 for a root).  With ``window`` > 0 a query sees
+    only the visible keys whose logical (root-to-leaf path) position is
+    within ``window`` of its own ("Context Parallelism in ART", section 06)."""
     seg: np.ndarray
     parent: np.ndarray
+    window: int = 0
 
 
 def _as_array(x):
@@ -183,7 +188,7 @@ def attention(Q, K, V, qpos, kpos, mask=Causal(), scale: Optional[float] = None,
                               q.ctypes.data, nq * d, d, k.ctypes.data, nk * d, d,
                               v.ctypes.data, nk * dv, dv,
                               qpos.ctypes.data, kpos.ctypes.data, kind, seg_p, n_pos,
-                              par_p, n_seg, float(scale),
+                              par_p, n_seg, int(getattr(mask, "window", 0)), float(scale),
                               rows_arr.ctypes.data if rows_arr is not None else None, n_rows,
                               O.ctypes.data, L.ctypes.data, int(n_threads))
     if rc != 0:

@@ -82,6 +82,31 @@ static int visible(int kind, const int32_t* seg, const int32_t* parent, int32_t 
 }
 
 /*
+ * Logical positions of a packed tree ("Context Parallelism in ART", section
+ * 06: position IDs follow the root-to-leaf path): lp[x] = the number of tokens
+ * of the strict ancestor segments of seg(x) plus the number of earlier tokens
+ * of seg(x) itself.  Counted plainly over the storage order (no assumption on
+ * how segments are laid out).  Returns 0, or -1 on allocation failure.
+ */
+static int logical_positions(const int32_t* seg, int64_t n_pos, const int32_t* parent, int32_t n_seg,
+                             int64_t* lp) {
+    int64_t* len = (int64_t*)calloc((size_t)(n_seg > 0 ? n_seg : 1), sizeof(int64_t));
+    int64_t* seen = (int64_t*)calloc((size_t)(n_seg > 0 ? n_seg : 1), sizeof(int64_t));
+    if (!len || !seen) { free(len); free(seen); return -1; }
+    for (int64_t x = 0; x < n_pos; ++x) len[seg[x]] += 1;
+    for (int64_t x = 0; x < n_pos; ++x) {
+        int64_t anc = 0;
+        for (int32_t a = 0; a < n_seg; ++a)
+            if (is_strict_ancestor(parent, n_seg, a, seg[x])) anc += len[a];
+        lp[x] = anc + seen[seg[x]];
+        seen[seg[x]] += 1;
+    }
+    free(len);
+    free(seen);
+    return 0;
+}
+
+/*
  * oracle_attention: for each head h and each selected query row, attention
  * over the keys the predicate makes visible.
  *
@@ -101,9 +126,10 @@ int oracle_attention(int64_t H, int64_t nq, int64_t nk, int64_t d, int64_t dv, i
                      const int64_t* qpos, const int64_t* kpos,
                      int kind, const int32_t* seg, int64_t n_pos,
                      const int32_t* parent, int32_t n_seg,
-                     double scale, const int64_t* rows, int64_t n_rows,
+                     int64_t window, double scale, const int64_t* rows, int64_t n_rows,
                      double* O, double* L, int n_threads) {
-    if (H < 0 || nq < 0 || nk < 0 || d <= 0 || dv <= 0) return -1;
+    if (H < 0 || nq < 0 || nk < 0 || d <= 0 || dv <= 0 || window < 0) return -1;
+    if (window > 0 && kind == OR_FULL) return -1;
     if (!rows) n_rows = nq;
     if (kind == OR_TREE) {
         for (int64_t j = 0; j < nk; ++j)
@@ -112,6 +138,15 @@ int oracle_attention(int64_t H, int64_t nq, int64_t nk, int64_t d, int64_t dv, i
             int64_t i = rows ? rows[r] : r;
             if (i < 0 || i >= nq || qpos[i] < 0 || qpos[i] >= n_pos) return -1;
         }
+    }
+    /* sliding window ("Context Parallelism in ART", section 06): a query sees
+     * only the keys whose logical position is within `window` tokens of its
+     * own, the current token included; causal logical positions are the
+     * global positions themselves */
+    int64_t* lp = NULL;
+    if (window > 0 && kind == OR_TREE) {
+        lp = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_pos > 0 ? n_pos : 1));
+        if (!lp || logical_positions(seg, n_pos, parent, n_seg, lp) != 0) { free(lp); return -1; }
     }
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -131,8 +166,14 @@ int oracle_attention(int64_t H, int64_t nq, int64_t nk, int64_t d, int64_t dv, i
             for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
             /* the visible key set A, in ascending key index */
             int64_t n_vis = 0;
-            for (int64_t j = 0; j < nk; ++j)
-                if (visible(kind, seg, parent, n_seg, qpos[i], kpos[j])) idx[n_vis++] = j;
+            for (int64_t j = 0; j < nk; ++j) {
+                if (!visible(kind, seg, parent, n_seg, qpos[i], kpos[j])) continue;
+                if (window > 0) {
+                    int64_t lq = lp ? lp[qpos[i]] : qpos[i], lk = lp ? lp[kpos[j]] : kpos[j];
+                    if (lq - lk >= window) continue;
+                }
+                idx[n_vis++] = j;
+            }
             if (n_vis == 0) {
                 L[h * n_rows + r] = -INFINITY;
                 continue;
@@ -163,6 +204,7 @@ int oracle_attention(int64_t H, int64_t nq, int64_t nk, int64_t d, int64_t dv, i
         free(s);
         free(idx);
     }
+    free(lp);
     return 0;
 }
 

@@ -23,6 +23,9 @@ MUTANTS = {
                             "widen(V, dtype, h * v_sh + j * v_st + c)"),
     "scale_dropped": ("s[a] = acc * scale;", "s[a] = acc;"),
     "output_unnormalised": ("double p = exp(s[a] - lse);", "double p = exp(s[a] - m);"),
+    "window_off_by_one": ("if (lq - lk >= window) continue;", "if (lq - lk > window) continue;"),
+    "window_on_storage_positions": ("int64_t lq = lp ? lp[qpos[i]] : qpos[i], lk = lp ? lp[kpos[j]] : kpos[j];",
+                                    "int64_t lq = qpos[i], lk = kpos[j];"),
     "sink_weight_inverted": ("double w = (l == -INFINITY) ? 0.0 : exp(l - lt);",
                              "double w = (l == -INFINITY) ? 0.0 : exp(lt - l);"),
     "sink_mass_dropped": ("m + log(exp(l - m) + exp(a[h] - m));", "m + log(exp(l - m));"),

@@ -28,11 +28,13 @@ def _rand(rng, *shape):
 # ----------------------------------------------------------------------------
 # helpers that do not go through the reference's predicate
 # ----------------------------------------------------------------------------
-def _trajectory_mask(seg, parent):
+def _trajectory_mask(seg, parent, window=0):
     """Dense visibility built from root-to-leaf trajectories: a packed tree
     must behave as every trajectory run separately as a causal sequence
     (Context Parallelism in ART, section 01).  M[q, k] is True iff some
-    trajectory contains both and k comes no later than q in it."""
+    trajectory contains both and k comes no later than q in it (and, with a
+    window, fewer than `window` tokens before it in that trajectory:
+    section 06, sliding windows on the root-to-leaf path)."""
     seg = np.asarray(seg)
     parent = np.asarray(parent)
     n_seg = len(parent)
@@ -52,7 +54,8 @@ def _trajectory_mask(seg, parent):
         path.reverse()
         toks = np.concatenate([np.flatnonzero(seg == s) for s in path])
         for a in range(len(toks)):
-            M[toks[a], toks[: a + 1]] = True
+            lo = 0 if window <= 0 else max(0, a - window + 1)
+            M[toks[a], toks[lo: a + 1]] = True
     return M
 
 
@@ -521,3 +524,63 @@ def test_sink_special_cases():
     assert Ls[0, 0] == pytest.approx(1.5 + math.log(2.0), abs=1e-15)
     assert np.allclose(Os[0, 0], 0.5 * O[0, 0], atol=1e-15)
     assert Ls[0, 1] == 1.5 and np.all(Os[0, 1] == 0)              # no visible key: all mass is the sink's
+
+
+
+# ----------------------------------------------------------------------------
+# sliding window on logical (root-to-leaf) positions ("Context Parallelism in
+# ART", section 06)
+# ----------------------------------------------------------------------------
+def test_tiny_tree_window_from_page():
+    g = _golden("tiny_tree.json")
+    seg, parent = workloads.tiny_tree()
+    n = len(seg)
+    O, L = _visible_sets_via_oracle(n, oracle.Tree(seg, parent, window=3))
+    for q, keys in g["window3_visible"].items():
+        assert np.flatnonzero(O[int(q)] > 0).tolist() == keys
+    # without a window a query sees its logical position + 1 keys
+    O, L = _visible_sets_via_oracle(n, oracle.Tree(seg, parent))
+    for q, lpos in g["logical_position"].items():
+        assert round(math.exp(L[int(q)])) == lpos + 1
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("window", [1, 2, 5, 20])
+def test_window_vs_trajectory_bruteforce(seed, window):
+    rng = np.random.default_rng(100 + seed)
+    seg, parent = _random_tree(rng, 7)
+    n = len(seg)
+    M = _trajectory_mask(seg, parent, window)
+    Q, K, V = _rand(rng, 1, n, 8), _rand(rng, 1, n, 8), _rand(rng, 1, n, 8)
+    pos = np.arange(n)
+    O, L = oracle.attention(Q, K, V, pos, pos, oracle.Tree(seg, parent, window=window), 0.3)
+    Od, Ld = _dense_attention(Q[0], K[0], V[0], M, 0.3)
+    assert np.abs(O[0] - Od).max() <= 1e-12 and np.abs(L[0] - Ld).max() <= 1e-12
+
+
+@pytest.mark.parametrize("window", [1, 7, 64])
+def test_causal_window_vs_torch_sdpa(window):
+    import torch
+    rng = np.random.default_rng(7)
+    n, d = 96, 16
+    Q, K, V = _rand(rng, 1, n, d), _rand(rng, 1, n, d), _rand(rng, 1, n, d)
+    pos = np.arange(n)
+    O, L = oracle.attention(Q, K, V, pos, pos, oracle.Causal(window=window))
+    i, j = np.meshgrid(pos, pos, indexing="ij")
+    band = torch.from_numpy((j <= i) & (i - j < window))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V), attn_mask=band)
+    S = torch.from_numpy(Q[0] @ K[0].T / math.sqrt(d)).masked_fill(~band, -float("inf"))
+    assert np.abs(O[0] - ref[0].numpy()).max() <= 1e-12
+    assert np.abs(L[0] - torch.logsumexp(S, dim=1).numpy()).max() <= 1e-12
+
+
+def test_window_covering_everything_is_no_window():
+    rng = np.random.default_rng(8)
+    seg, parent = _random_tree(rng, 6)
+    n = len(seg)
+    Q, K, V = _rand(rng, 1, n, 8), _rand(rng, 1, n, 8), _rand(rng, 1, n, 8)
+    pos = np.arange(n)
+    a = oracle.attention(Q, K, V, pos, pos, oracle.Tree(seg, parent))
+    b = oracle.attention(Q, K, V, pos, pos, oracle.Tree(seg, parent, window=n))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
