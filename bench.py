@@ -201,6 +201,38 @@ def gqa_ring(cp, workloads, torch, dev, seg, parent, N, flops, steps: int = 10):
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N, window: int = 4096, steps: int = 10):
+    """The 64K tree row and ring with a sliding window of `window` logical
+    (root-to-leaf) positions: the kernels skip the tiles outside the window.
+    FLOPs counted on the visible pairs of the windowed mask (exact, from
+    cpattn_ring_plan)."""
+    H, n, d = qd.shape
+    c = n // N
+    mask = cp.Mask.tree(seg, parent).with_window(window)
+    pairs = int(cp.ring_plan([c] * N, [(r * c, 1) for r in range(N)], mask).sum())
+    flops = 4.0 * d * H * pairs
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    Q, K, V = blk(qd), blk(kd), blk(vd)
+    pos = [(r * c, 1) for r in range(N)]
+    outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
+                torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    mask.free()
+    return {"workload": "tree64k ring of %d, sliding window of %d logical positions" % (N, window),
+            "visible_pairs_per_head": pairs, "ms_per_step": round(ms, 4),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +395,7 @@ def main():
     if not args.no_balance:
         result["load_balance"] = load_balance(cp, workloads, torch, dev)
         result["gqa"] = gqa_ring(cp, workloads, torch, dev, seg, parent, N, flops)
+        result["window"] = window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N)
 
     if not args.no_cpu:
         import oracle

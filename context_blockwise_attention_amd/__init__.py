@@ -69,6 +69,7 @@ def lib():
         L.cpattn_mask_causal.argtypes = [ctypes.c_int64, ctypes.POINTER(P)]
         L.cpattn_mask_tree.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, P, ctypes.POINTER(P)]
         L.cpattn_mask_free.argtypes = [P]
+        L.cpattn_mask_with_window.argtypes = [P, ctypes.c_int64, P, ctypes.POINTER(P)]
         L.cpattn_mask_npos.argtypes = [P]
         L.cpattn_mask_npos.restype = ctypes.c_int64
         L.cpattn_partial.argtypes = [ctypes.POINTER(_Tensor)] * 3 + [P, _PosMap, _PosMap, ctypes.c_float,
@@ -82,7 +83,7 @@ def lib():
         L.cpattn_apply_sink.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
         for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
                   "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan",
-                  "cpattn_apply_sink"):
+                  "cpattn_apply_sink", "cpattn_mask_with_window"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -155,6 +156,16 @@ class Mask:
         _check(lib().cpattn_mask_tree(seg.ctypes.data, seg.shape[0], par.ctypes.data, par.shape[0],
                                       _stream(stream), ctypes.byref(h)))
         return cls(h.value, int(seg.shape[0]), "tree")
+
+    def with_window(self, window: int, stream=None) -> "Mask":
+        """A new descriptor: this visibility restricted to keys within
+        ``window`` logical (root-to-leaf) positions of the query, itself
+        included."""
+        h = ctypes.c_void_p()
+        # a causal descriptor has no device arrays: no stream needed (host only)
+        st = 0 if (stream is None and not self.kind.startswith("tree")) else _stream(stream)
+        _check(lib().cpattn_mask_with_window(self.handle, int(window), st, ctypes.byref(h)))
+        return Mask(h.value, self.n_pos, self.kind + "+window%d" % int(window))
 
     @property
     def handle(self):

@@ -56,9 +56,12 @@ struct cpattn_mask {
     int64_t n_pos;
     std::vector<SegInfo> segs;    // host copy (tree)
     std::vector<int32_t> run_order;   // segments by run start (tree)
+    std::vector<int64_t> anc_len;     // tokens of the strict ancestors of each segment (tree)
+    int32_t window = 0;           // sliding window in logical positions (0 = none)
     int32_t* d_seg = nullptr;     // [n_pos]
     int32_t* d_end = nullptr;     // [n_pos]
     int4* d_segtab = nullptr;     // [n_seg]
+    int32_t* d_lpos = nullptr;    // [n_pos] logical positions (tree with a window)
 };
 
 extern "C" int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out) {
@@ -77,10 +80,12 @@ extern "C" int cpattn_mask_free(cpattn_mask* m) {
     hipError_t e1 = m->d_seg ? hipFree(m->d_seg) : hipSuccess;
     hipError_t e2 = m->d_end ? hipFree(m->d_end) : hipSuccess;
     hipError_t e3 = m->d_segtab ? hipFree(m->d_segtab) : hipSuccess;
+    hipError_t e4 = m->d_lpos ? hipFree(m->d_lpos) : hipSuccess;
     delete m;
     if (e1 != hipSuccess) return hip_fail(e1, "cpattn_mask_free");
     if (e2 != hipSuccess) return hip_fail(e2, "cpattn_mask_free");
     if (e3 != hipSuccess) return hip_fail(e3, "cpattn_mask_free");
+    if (e4 != hipSuccess) return hip_fail(e4, "cpattn_mask_free");
     return CPATTN_OK;
 }
 
@@ -154,6 +159,11 @@ extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int3
     m->n_pos = n_tok;
     m->segs = segs;
     m->run_order = order;
+    m->anc_len.assign((size_t)n_seg, 0);
+    for (int32_t sgi : order) {   // preorder: a parent's total is known before its children's
+        const int32_t p = segs[sgi].parent;
+        m->anc_len[sgi] = p < 0 ? 0 : m->anc_len[p] + (segs[p].run_end - segs[p].run_start);
+    }
     std::vector<int32_t> end((size_t)n_tok);
     for (int64_t x = 0; x < n_tok; ++x) end[x] = segs[seg_id[x]].subtree_end;
     std::vector<int4> tab((size_t)n_seg);
@@ -187,6 +197,53 @@ extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int3
         return hip_fail(e, "cpattn_mask_tree: upload");
     }
     *out = m;
+    return CPATTN_OK;
+}
+
+// A descriptor with the same visibility as m plus a sliding window on logical
+// (root-to-leaf) positions.  The new descriptor owns copies of m's device
+// arrays and, for a tree, the logical position of every physical position.
+extern "C" int cpattn_mask_with_window(const cpattn_mask* m, int64_t window, void* stream, cpattn_mask** out) {
+    const char* who = "cpattn_mask_with_window";
+    if (!out) return fail(CPATTN_EINVAL, "%s: out is NULL", who);
+    *out = nullptr;
+    if (!m) return fail(CPATTN_EINVAL, "%s: mask is NULL", who);
+    if (window < 1 || window > (1 << 30)) return fail(CPATTN_EINVAL, "%s: window %lld out of range [1, 2^30]", who,
+                                                        (long long)window);
+    cpattn_mask* w = new (std::nothrow) cpattn_mask();
+    if (!w) return fail(CPATTN_ENOMEM, "%s: out of host memory", who);
+    w->kind = m->kind;
+    w->n_pos = m->n_pos;
+    w->segs = m->segs;
+    w->run_order = m->run_order;
+    w->anc_len = m->anc_len;
+    w->window = (int32_t)window;
+    if (m->kind == kTree) {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        const size_t nb = sizeof(int32_t) * (size_t)std::max<int64_t>(m->n_pos, 1);
+        const size_t tb = sizeof(int4) * std::max<size_t>(m->segs.size(), 1);
+        std::vector<int32_t> lpos((size_t)m->n_pos);
+        for (int32_t sg : m->run_order)
+            for (int32_t x = m->segs[sg].run_start; x < m->segs[sg].run_end; ++x)
+                lpos[x] = (int32_t)(m->anc_len[sg] + x - m->segs[sg].run_start);
+        hipError_t e;
+        if ((e = hipMalloc(&w->d_seg, nb)) != hipSuccess || (e = hipMalloc(&w->d_end, nb)) != hipSuccess ||
+            (e = hipMalloc(&w->d_segtab, tb)) != hipSuccess || (e = hipMalloc(&w->d_lpos, nb)) != hipSuccess) {
+            cpattn_mask_free(w);
+            return fail(CPATTN_ENOMEM, "%s: hipMalloc: %s", who, hipGetErrorString(e));
+        }
+        if ((e = hipMemcpyAsync(w->d_seg, m->d_seg, nb, hipMemcpyDeviceToDevice, st)) != hipSuccess ||
+            (e = hipMemcpyAsync(w->d_end, m->d_end, nb, hipMemcpyDeviceToDevice, st)) != hipSuccess ||
+            (e = hipMemcpyAsync(w->d_segtab, m->d_segtab, tb, hipMemcpyDeviceToDevice, st)) != hipSuccess ||
+            (m->n_pos > 0 &&
+             (e = hipMemcpyAsync(w->d_lpos, lpos.data(), sizeof(int32_t) * (size_t)m->n_pos, hipMemcpyHostToDevice,
+                                 st)) != hipSuccess) ||
+            (e = hipStreamSynchronize(st)) != hipSuccess) {
+            cpattn_mask_free(w);
+            return hip_fail(e, "cpattn_mask_with_window: upload");
+        }
+    }
+    *out = w;
     return CPATTN_OK;
 }
 
@@ -228,8 +285,12 @@ static int check_posmap(cpattn_posmap p, int64_t n, const cpattn_mask* m, const 
 
 // Does any query of the block see any key of the block?  Exact for both masks
 // (per segment, the smallest key position gives the widest chance).
+static int64_t pair_count(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk,
+                          int64_t step);
+
 static bool pair_nonempty(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
     if (nq == 0 || nk == 0) return false;
+    if (m->window > 0) return pair_count(m, qp, nq, kp, nk, 1) > 0;   // exact, per query row
     const int64_t qmax = qp.base + qp.stride * (nq - 1);
     auto first_query_at_or_after = [&](int64_t x) -> int64_t {
         if (x <= qp.base) return qp.base;
@@ -270,17 +331,25 @@ static int64_t pair_count(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cp
     int64_t sum = 0;
     for (int64_t i = 0; i < nq; i += step) {
         const int64_t y = qp.base + qp.stride * i;
+        // keys of a run of segment s (positions [a, b]) whose logical position
+        // (x - run_start + anc_len) is within the window of the query's
+        const int64_t W = m->window;
         if (m->kind == kCausal) {
-            sum += keys_in_range(kp, nk, 0, y);
+            sum += keys_in_range(kp, nk, W > 0 ? std::max<int64_t>(0, y - W + 1) : 0, y);
             continue;
         }
         // segment of position y: the last run starting at or before y
         auto it = std::upper_bound(m->run_order.begin(), m->run_order.end(), y,
                                    [&](int64_t v, int32_t seg) { return v < m->segs[seg].run_start; });
         int32_t sg = *(it - 1);
-        int64_t c = keys_in_range(kp, nk, m->segs[sg].run_start, y);
+        const int64_t ly = m->anc_len[sg] + y - m->segs[sg].run_start;
+        auto clip = [&](int32_t s2) {   // first position of s2's run inside the window
+            const int64_t lbase = m->segs[s2].run_start - m->anc_len[s2];
+            return W > 0 ? std::max<int64_t>(m->segs[s2].run_start, ly - W + 1 + lbase) : (int64_t)m->segs[s2].run_start;
+        };
+        int64_t c = keys_in_range(kp, nk, clip(sg), y);
         for (int32_t a = m->segs[sg].parent; a >= 0; a = m->segs[a].parent)
-            c += keys_in_range(kp, nk, m->segs[a].run_start, m->segs[a].run_end - 1);
+            c += keys_in_range(kp, nk, clip(a), m->segs[a].run_end - 1);
         sum += c;
     }
     return sum * step;
@@ -295,19 +364,20 @@ static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, 
 // ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
-template <typename T, int D, int BN>
+template <typename T, int D, int BN, bool WIN>
 static int launch_partial_t(LaunchArgs& a, hipStream_t st) {
     using TL = Tile<T, D, BN>;
     const int smem = 2 * TL::STAGE_BYTES;
+    const auto kern = partial_attention_kernel<T, D, BN, WIN>;
     static bool attr_set = false;   // per instantiation; the attribute is per function
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&partial_attention_kernel<T, D, BN>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
         attr_set = true;
     }
     const int grid = (a.total_wg + 7) / 8 * 8;
-    hipLaunchKernelGGL((partial_attention_kernel<T, D, BN>), dim3(grid), dim3(kThreads), smem, st, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "partial attention launch");
     return CPATTN_OK;
@@ -318,11 +388,11 @@ static int launch_partial_t(LaunchArgs& a, hipStream_t st) {
 constexpr int kBf16BN = 64;
 constexpr int kBf16PF = 2;
 
-template <int D>
+template <int D, bool WIN>
 static int launch_bf16(LaunchArgs& a, hipStream_t st) {
     using TT = PPTile<D, kBf16BN, kBf16PF>;
-    const auto kern = attn_bf16_pp_kernel<D, kBf16BN, kBf16PF>;
-    const int smem = TT::LDS_BYTES;
+    const auto kern = attn_bf16_pp_kernel<D, kBf16BN, kBf16PF, WIN>;
+    const int smem = WIN ? TT::LDS_BYTES_WIN : TT::LDS_BYTES;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -337,14 +407,17 @@ static int launch_bf16(LaunchArgs& a, hipStream_t st) {
     return CPATTN_OK;
 }
 
+// one instantiation per (dtype, head dim, window or not); the windowed ones
+// differ only in the tile walk and the elementwise mask
 static int launch_partial(LaunchArgs& a, int dtype, int d, hipStream_t st) {
     if (a.total_wg == 0) return CPATTN_OK;
+    const bool win = a.mask.window > 0;
     if (dtype == CPATTN_BF16) {
-        if (d == 128) return launch_bf16<128>(a, st);
-        return launch_bf16<64>(a, st);
+        if (d == 128) return win ? launch_bf16<128, true>(a, st) : launch_bf16<128, false>(a, st);
+        return win ? launch_bf16<64, true>(a, st) : launch_bf16<64, false>(a, st);
     }
-    if (d == 128) return launch_partial_t<float, 128, 32>(a, st);
-    return launch_partial_t<float, 64, 32>(a, st);
+    if (d == 128) return win ? launch_partial_t<float, 128, 32, true>(a, st) : launch_partial_t<float, 128, 32, false>(a, st);
+    return win ? launch_partial_t<float, 64, 32, true>(a, st) : launch_partial_t<float, 64, 32, false>(a, st);
 }
 
 static MaskArgs mask_args(const cpattn_mask* m) {
@@ -354,6 +427,8 @@ static MaskArgs mask_args(const cpattn_mask* m) {
     ma.seg = m->d_seg;
     ma.end = m->d_end;
     ma.segtab = m->d_segtab;
+    ma.lpos = m->d_lpos;
+    ma.window = m->window;
     return ma;
 }
 

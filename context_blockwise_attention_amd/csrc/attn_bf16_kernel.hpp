@@ -134,11 +134,14 @@ struct PPTile {
     static constexpr int V_OFF = NBUF * TILE_BYTES;
     static constexpr int E_OFF = 2 * NBUF * TILE_BYTES;
     static constexpr int LDS_BYTES = E_OFF + NEB * BN * 4;
+    // sliding window on a tree: the keys' logical positions follow the horizons
+    static constexpr int L_OFF = LDS_BYTES;
+    static constexpr int LDS_BYTES_WIN = L_OFF + NEB * BN * 4;
     static_assert(NI >= 1 && BN % 64 == 0, "tile shape");
     static_assert(PF == 2, "the tile loop issues loads two iterations ahead");
 };
 
-template <int D, int BN_, int PF_>
+template <int D, int BN_, int PF_, bool WIN>
 __global__ void __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_pp_kernel(const LaunchArgs args) {
     using TT = PPTile<D, BN_, PF_>;
@@ -176,6 +179,20 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     const bool tree = args.mask.kind == kTree;
     // last key index of the block at or before this query's position
     const int jlim = min(J.n_k - 1, ypos < J.kbase ? -1 : (ypos - J.kbase) / J.kstride);
+    // Sliding window (WIN): a key is visible only if its logical position is
+    // above the query's minus the window.  Causal: logical = physical, so the
+    // window is a lower key-index bound jlo per query.  Tree: the query's
+    // logical position ly, compared with each key's (staged in LDS).
+    int jlo = 0, ly = 0;
+    if (WIN) {
+        if (tree) {
+            const auto lr = make_rsrc(args.mask.lpos, args.mask.n_pos * 4);
+            ly = qi < J.n_q ? (int)__builtin_amdgcn_raw_buffer_load_b32(lr, ypos * 4, 0, 0) : 0;
+        } else {
+            const int lowest = ypos - args.mask.window + 1 - J.kbase;   // lowest visible key position, block-relative
+            jlo = lowest <= 0 ? 0 : (lowest + J.kstride - 1) / J.kstride;
+        }
+    }
 
     const __bf16* qh = reinterpret_cast<const __bf16*>(J.q) + head * J.q_sh;
     const int kv_head = head / J.kv_group;   // grouped-query attention: query heads share a K/V head
@@ -207,6 +224,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     const i32x4 k_rsrc = sgpr_rsrc(kh, (J.n_k - 1) * J.k_st * 2 + D * 2);
     const i32x4 v_rsrc = sgpr_rsrc(vh, (J.n_k - 1) * J.v_st * 2 + D * 2);
     const i32x4 e_rsrc = sgpr_rsrc(args.mask.end, args.mask.n_pos * 4);
+    const i32x4 l_rsrc = WIN ? sgpr_rsrc(args.mask.lpos, args.mask.n_pos * 4) : i32x4{};
     // a tile is loaded by the four waves of group 0: wave w fills the 1 KB
     // blocks b = 4i + w; the horizons by its first wave
     const int wl = wave & 3;
@@ -223,9 +241,15 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         for (int i = 0; i < TT::NI; ++i) dma_b128(rsrc, voffs[i] + tile_bytes, lds_addr(dst + (i * 4 + wl) * 1024));
     };
     // horizons: the group's first BN/64 waves each load 64 of the tile's entries
-    auto issue_e = [&](int tile, lds_byte* dst) {
-        if (wl < BN / 64)
-            dma_b32(e_rsrc, (kblk.kbase + kblk.kstride * (tile * BN + wl * 64 + lane)) * 4, lds_addr(dst + wl * 256));
+    auto issue_e = [&](int tile, int slot) {
+        constexpr int W64 = BN / 64;
+        static_assert(!WIN || 2 * W64 <= 4, "horizon and logical-position loads fit the loading group");
+        if (wl < W64)
+            dma_b32(e_rsrc, (kblk.kbase + kblk.kstride * (tile * BN + wl * 64 + lane)) * 4,
+                    lds_addr(lds + TT::E_OFF + (slot % TT::NEB) * BN * 4 + wl * 256));
+        else if (WIN && wl < 2 * W64)
+            dma_b32(l_rsrc, (kblk.kbase + kblk.kstride * (tile * BN + (wl - W64) * 64 + lane)) * 4,
+                    lds_addr(lds + TT::L_OFF + (slot % TT::NEB) * BN * 4 + (wl - W64) * 256));
     };
     auto kbuf = [&](int s) { return lds + TT::K_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
     auto vbuf = [&](int s) { return lds + TT::V_OFF + (s % TT::NBUF) * TT::TILE_BYTES; };
@@ -297,6 +321,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             // ypos < end[kpos(j)]; jl below is the key's index in the tile.
             // Branch-free: one compare (two for trees) and a select per score.
             const int lim = jlim - tile * BN - 8 * g;
+            const int lo = jlo - tile * BN - 8 * g;   // window (causal)
             if (tree) {
                 const auto* ep = reinterpret_cast<const __attribute__((address_space(3))) int*>(e_lds) + 8 * g;
 #pragma unroll
@@ -307,9 +332,16 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                         int ends[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) ends[e] = ep[jl0 + e];
+                        int lks[8];
+                        if (WIN) {
+                            const auto* lq = ep + (TT::L_OFF - TT::E_OFF) / 4;   // same slot, logical positions
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) lks[e] = lq[jl0 + e];
+                        }
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const bool vis = (jl0 + e <= lim) & (ypos < ends[e]);
+                            bool vis = (jl0 + e <= lim) & (ypos < ends[e]);
+                            if (WIN) vis &= ly - lks[e] < args.mask.window;
                             s[kb][hf * 8 + e] = vis ? s[kb][hf * 8 + e] : -INFINITY;
                         }
                     }
@@ -320,7 +352,8 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int jl = kb * 32 + (i >> 3) * 16 + (i & 7);
-                        s[kb][i] = jl <= lim ? s[kb][i] : -INFINITY;
+                        const bool vis = WIN ? (jl <= lim) & (jl >= lo) : jl <= lim;
+                        s[kb][i] = vis ? s[kb][i] : -INFINITY;
                     }
             }
         }
@@ -405,7 +438,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
         if (group != G) continue;
-        TileCursor<BN> cur;
+        TileCursor<BN, WIN> cur;
         cur.init(kblk, args.mask, y0, y1);
         // tiles t, t+1, t+2 of the walk (h_*: whether they exist)
         int t_cur = 0, f_cur = 0, t_nxt = 0, f_nxt = 0, t_n2 = 0, f_n2 = 0;
@@ -413,14 +446,14 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         bool h_nxt = cur.next(kblk, args.mask, y1, &t_nxt, &f_nxt);
         bool h_n2 = false;
         // horizon loads per tile of this wave (group 0 loads them)
-        const int e_loads = (G == 0 && tree && wl < BN / 64) ? 1 : 0;
+        const int e_loads = (G == 0 && tree && wl < (WIN ? 2 : 1) * (BN / 64)) ? 1 : 0;
         // this wave's loads issued in the current iteration (they may stay in
         // flight across the next barrier)
         int pending = 0;
         // K/E of tile t+2 (group 0, after its tile walk has produced it)
         auto issue_ke = [&](int tile, int s) {
             issue_kv(k_rsrc, voffk, k_st, tile, kbuf(s));
-            if (tree) issue_e(tile, ebuf(s));
+            if (tree) issue_e(tile, s);
         };
         // prologue: group 0 loads K(0), E(0), V(0), K(1), E(1); only K(0) and
         // E(0) must land before barrier 0

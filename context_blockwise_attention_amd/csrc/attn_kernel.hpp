@@ -70,8 +70,10 @@ struct MaskArgs {
     const int32_t* seg;     // [n_pos] segment of each position (tree only)
     const int4* segtab;     // [n_seg] {run_start, run_end, parent, subtree_end}
     const int32_t* end;     // [n_pos] subtree end of each position (tree only)
+    const int32_t* lpos;    // [n_pos] logical (root-to-leaf) position (tree with a window only)
     int32_t n_pos;
     int32_t kind;
+    int32_t window;         // sliding window in logical positions (0 = none)
 };
 
 struct LaunchArgs {
@@ -161,7 +163,7 @@ struct Tile {
     static constexpr int VS = BN + Elem<T>::kPad;  // V^T row stride (elements) in LDS
     static constexpr int K_ELEMS = BN * KS;
     static constexpr int V_ELEMS = D * VS;
-    static constexpr int STAGE_BYTES = (K_ELEMS + V_ELEMS) * (int)sizeof(T) + BN * 4;
+    static constexpr int STAGE_BYTES = (K_ELEMS + V_ELEMS) * (int)sizeof(T) + 2 * BN * 4;   // + horizons, logical positions
     static constexpr int K_CHUNKS = BN * D / EPC;            // 16-byte chunks of a K tile
     static constexpr int K_PER_THREAD = (K_CHUNKS + kThreads - 1) / kThreads;
     static constexpr int KG = BN / 4;                          // 4-key groups of a V tile
@@ -242,21 +244,40 @@ __device__ __forceinline__ i32x4 seg_entry(const MaskArgs& M, int s) {
 // (every key visible to every query row of the tile).  Both are decided once
 // per range, so producing a tile is a compare and a decrement; moving to the
 // next range is the rare path.
-template <int BN>
+//
+// With a sliding window (WIN; "Context Parallelism in ART", section 06: a
+// query sees the keys within `window` tokens of its logical, root-to-leaf,
+// position), each range is first clipped to the keys some query of the tile
+// can reach (logical position >= the tile's lowest query position - window
+// + 1), and a tile is full only if its first key lies within the window of
+// the tile's highest query position.  Inside one segment's run the logical
+// position is the physical one minus the run's offset `lbase` (run start
+// minus its logical position; 0 for a causal mask).
+template <int BN, bool WIN = false>
 struct TileCursor {
     int t;        // next tile to emit; the range is exhausted when t < t_lo
     int t_lo;     // lowest tile of the current range
     int fa, fb;   // full tiles of the current range (none when fa > fb)
     int seg;      // segment whose run is the current range (tree); -1 = no further range
+    int lq_min, lq_max;   // WIN: bounds of the query tile's logical positions
 
     __device__ __forceinline__ static int ceil_div(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
     __device__ __forceinline__ static int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+    __device__ __forceinline__ static int64_t ceil_div64(int64_t a, int64_t b) {
+        return a >= 0 ? (a + b - 1) / b : -((-a) / b);
+    }
 
     // Enters the key positions [pa, pb] inside the block.  A tile is full if
     // it lies inside the range, full_ok holds (every key's subtree contains
-    // the whole query tile) and its last key index is at most j_last.  False
+    // the whole query tile) and its last key index is at most j_last (and,
+    // with a window, its first key is within reach of every query).  False
     // (state unchanged) if no tile below the ones emitted is left.
-    __device__ __forceinline__ bool set_range(int pa, int pb, bool full_ok, int j_last, const KeyBlock& J) {
+    __device__ __forceinline__ bool set_range(int pa, int pb, bool full_ok, int j_last, const KeyBlock& J,
+                                              const MaskArgs& M, int lbase) {
+        if (WIN) {
+            pa = (int)max((int64_t)pa, (int64_t)lq_min - M.window + 1 + lbase);
+            if (pa > pb) return false;
+        }
         int lo, hi;
         if (J.kstride == 1) {
             lo = pa - J.kbase;
@@ -277,7 +298,18 @@ struct TileCursor {
         // (j_last + 1 <= 0 leaves fb < 0: no tile full)
         fa = full_ok ? (lo + BN - 1) / BN : 1;
         fb = full_ok ? min(hi + 1, j_last + 1) / BN - 1 : 0;
+        if (WIN && full_ok) {
+            // first key index within the window of every query of the tile
+            const int64_t thr = (int64_t)lq_max - M.window + 1 + lbase;
+            const int64_t jthr = max((int64_t)0, ceil_div64(thr - J.kbase, J.kstride));
+            fa = (int)min((int64_t)0x3fffffff, max((int64_t)fa, (jthr + BN - 1) / BN));
+        }
         return true;
+    }
+
+    // run offset of segment s's run: run start minus its logical position
+    __device__ __forceinline__ static int run_lbase(const MaskArgs& M, int run_start) {
+        return run_start - ((const __attribute__((address_space(4))) int32_t*)M.lpos)[run_start];
     }
 
     // The first range: the query tile's own run up to y1 (its keys after y0
@@ -288,12 +320,26 @@ struct TileCursor {
         seg = -1;
         const int j_own = J.kstride == 1 ? y0 - J.kbase : floor_div(y0 - J.kbase, J.kstride);
         if (M.kind == kCausal) {
-            set_range(0, y1, true, j_own, J);
+            if (WIN) {
+                lq_min = y0;
+                lq_max = y1;
+            }
+            set_range(0, y1, true, j_own, J, M, 0);
             return;
         }
         seg = ((const __attribute__((address_space(4))) int32_t*)M.seg)[y0];
         const i32x4 st = seg_entry(M, seg);
-        set_range(st.x, y1, st.w > y1, j_own, J);
+        int lbase = 0;
+        if (WIN) {
+            const auto* lp = (const __attribute__((address_space(4))) int32_t*)M.lpos;
+            const bool one_seg = ((const __attribute__((address_space(4))) int32_t*)M.seg)[y1] == seg;
+            // a tile that crosses a segment boundary keeps every key in reach
+            // and has no full tile (its positions are not one logical run)
+            lq_min = one_seg ? lp[y0] : -(1 << 30);
+            lq_max = one_seg ? lp[y1] : (1 << 30);
+            lbase = run_lbase(M, st.x);
+        }
+        set_range(st.x, y1, st.w > y1, j_own, J, M, lbase);
     }
 
     // Moves to the runs of the ancestor segments until one has a tile left.
@@ -302,7 +348,7 @@ struct TileCursor {
             seg = seg_entry(M, seg).z;
             if (seg < 0) break;
             const i32x4 sp = seg_entry(M, seg);
-            if (set_range(sp.x, sp.y - 1, sp.w > y1, 0x7ffffffe, J)) return true;
+            if (set_range(sp.x, sp.y - 1, sp.w > y1, 0x7ffffffe, J, M, WIN ? run_lbase(M, sp.x) : 0)) return true;
         }
         return false;
     }
@@ -380,7 +426,7 @@ __device__ __forceinline__ void write_result(const JobArgs& J, int head, int qi,
 // ---------------------------------------------------------------------------
 // the register-staged kernel (fp32 inputs; the bf16 path is attn_bf16_kernel.hpp)
 // ---------------------------------------------------------------------------
-template <typename T, int D, int BN>
+template <typename T, int D, int BN, bool WIN>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 partial_attention_kernel(const LaunchArgs args) {
     using E = Elem<T>;
@@ -412,6 +458,18 @@ partial_attention_kernel(const LaunchArgs args) {
     // this lane's query row
     const int qi = q_first + wave * 32 + r32;
     const int ypos = J.qbase + J.qstride * qi;
+    // sliding window (see the bf16 kernel): causal -> lowest visible key
+    // index; tree -> the query's logical position
+    const bool tree_q = args.mask.kind == kTree;
+    int jlo = 0, ly = 0;
+    if (WIN) {
+        if (tree_q) {
+            ly = qi < J.n_q ? args.mask.lpos[ypos] : 0;
+        } else {
+            const int lowest = ypos - args.mask.window + 1 - J.kbase;
+            jlo = lowest <= 0 ? 0 : (lowest + J.kstride - 1) / J.kstride;
+        }
+    }
 
     const T* qh = reinterpret_cast<const T*>(J.q) + head * J.q_sh;
     const int kv_head = head / J.kv_group;
@@ -452,7 +510,7 @@ partial_attention_kernel(const LaunchArgs args) {
     //    LDS writes of one instruction fill consecutive 8-byte slots of a row.
     u32x4 kreg[TL::K_PER_THREAD];
     u32x4 vreg[TL::V_PER_THREAD][4];
-    int endreg = 0;
+    int endreg = 0, lreg = 0;
 
     const bool tree = args.mask.kind == kTree;
     auto stage_load = [&](int tile) {
@@ -478,6 +536,10 @@ partial_attention_kernel(const LaunchArgs args) {
         if (tree && tid < BN) {
             const int j = j0 + tid;
             endreg = j < J.n_k ? args.mask.end[J.kbase + J.kstride * j] : (int)0x80000000;
+        }
+        if (WIN && tree && tid >= BN && tid < 2 * BN) {
+            const int j = j0 + tid - BN;
+            lreg = j < J.n_k ? args.mask.lpos[J.kbase + J.kstride * j] : 0;
         }
     };
 
@@ -520,10 +582,11 @@ partial_attention_kernel(const LaunchArgs args) {
             }
         }
         if (tree && tid < BN) Es[tid] = endreg;
+        if (WIN && tree && tid >= BN && tid < 2 * BN) Es[tid] = lreg;   // Ls = Es + BN
     };
 
     // ---- tile walk ------------------------------------------------------------
-    TileCursor<BN> cur;
+    TileCursor<BN, WIN> cur;
     cur.init(kblk, args.mask, y0, y1);
     int tile, full;
     bool have = cur.next(kblk, args.mask, y1, &tile, &full);
@@ -563,6 +626,7 @@ partial_attention_kernel(const LaunchArgs args) {
                     const int j = tile * BN + jl;
                     bool vis = j < J.n_k && J.kbase + J.kstride * j <= ypos;
                     if (tree) vis = vis && ypos < Es[jl];
+                    if (WIN) vis = vis && (tree ? ly - Es[BN + jl] < args.mask.window : j >= jlo);
                     if (!vis) s[kb][i] = -INFINITY;
                 }
             }

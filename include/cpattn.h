@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 4
+#define CPATTN_VERSION_MINOR 5
 
 typedef enum {
     CPATTN_OK = 0,
@@ -106,6 +106,21 @@ int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out);
  * complete when the function returns (the host arrays may be freed). */
 int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
                      void* stream, cpattn_mask** out);
+
+/* Sliding-window attention on logical positions ("Context Parallelism in
+ * ART", section 06): a new descriptor with the visibility of `m` restricted
+ * to the keys whose logical position is within `window` tokens of the
+ * query's, the query included (logical position = position along the
+ * root-to-leaf path: the tokens of the strict ancestor segments plus the
+ * earlier tokens of the own segment; for a causal mask, the position itself).
+ * With window 3, query B8 of the section's tiny tree sees physical positions
+ * 3, 7, 8, not the last three physical addresses.  The new descriptor owns
+ * copies of m's device arrays (m may be freed first) and is used like any
+ * other; partial, ring, plan and merge calls honour its window, and the
+ * kernels skip tiles outside it.  1 <= window <= 2^30, else EINVAL; ENOMEM /
+ * EDEVICE on allocation or upload failure (enqueued on `stream`, complete on
+ * return). */
+int cpattn_mask_with_window(const cpattn_mask* m, int64_t window, void* stream, cpattn_mask** out);
 
 /* Releases a descriptor and its device arrays.  The caller guarantees that no
  * enqueued work still uses it.  NULL is accepted. */

@@ -104,3 +104,32 @@ def test_plan_rejects_bad_arguments(cp):
     with pytest.raises(cp.CpattnError) as e:
         cp.ring_plan([-1, 8], [(0, 1), (8, 1)], m)
     assert e.value.code == cp.EINVAL
+
+
+@pytest.mark.parametrize("window", [1, 5, 23])
+@pytest.mark.parametrize("C", [1, 2])
+def test_plan_with_causal_window(cp, window, C):
+    """Sliding window on a causal sequence ("Context Parallelism in ART",
+    section 06): the plan counts only pairs with y - window < x <= y."""
+    s, N = 64, 4
+    m = cp.Mask.causal(s).with_window(window)
+    c = s // (N * C)
+    chunks = list(range(N)) if C == 1 else [ch for r in range(N) for ch in (r, 2 * N - 1 - r)]
+    w = cp.ring_plan([c] * (N * C), [(ch * c, 1) for ch in chunks], m, chunks_per_rank=C)
+    y, x = np.meshgrid(np.arange(s), np.arange(s), indexing="ij")
+    vis = (x <= y) & (y - x < window)
+    for r in range(N):
+        for kk in range(N):
+            b = (r - kk) % N
+            qs = np.concatenate([np.arange(ch * c, (ch + 1) * c) for ch in chunks[r * C:(r + 1) * C]])
+            ks = np.concatenate([np.arange(ch * c, (ch + 1) * c) for ch in chunks[b * C:(b + 1) * C]])
+            assert w[r, kk] == int(vis[np.ix_(qs, ks)].sum())
+    assert int(w.sum()) == int(vis.sum())
+
+
+def test_window_rejects_bad_arguments(cp):
+    m = cp.Mask.causal(16)
+    for bad in (0, -3, (1 << 30) + 1):
+        with pytest.raises(cp.CpattnError) as e:
+            m.with_window(bad)
+        assert e.value.code == cp.EINVAL
