@@ -75,6 +75,15 @@ def _load():
                                          i64, ctypes.c_double, p, i64, p, p, ctypes.c_int]
         lib.oracle_merge2.restype = None
         lib.oracle_merge2.argtypes = [i64, i64, p, p, p, p]
+        lib.oracle_attention_backward.restype = ctypes.c_int
+        lib.oracle_attention_backward.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                                  p, i64, i64, p, i64, i64, p, i64, i64,
+                                                  p, p, ctypes.c_int, p, i64, p, ctypes.c_int32,
+                                                  i64, ctypes.c_double, p, i64, p, p, p, p, p, p]
+        lib.oracle_merge_backward.restype = None
+        lib.oracle_merge_backward.argtypes = [ctypes.c_int, p, p, i64, i64, p, p, p, p, p, p]
+        lib.oracle_sink_backward.restype = None
+        lib.oracle_sink_backward.argtypes = [i64, i64, i64, p, p, p, p, p, p, p]
         lib.oracle_apply_sink.restype = None
         lib.oracle_apply_sink.argtypes = [i64, i64, i64, p, p, p]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -258,3 +267,101 @@ def ring(Q_r, q_pos, K_blocks, V_blocks, kv_pos, rank: int, mask=Causal(), scale
         if keep_rounds:
             rounds.append((b, part, run))
     return (run[0], run[1], rounds) if keep_rounds else run
+
+
+
+def _mask_fields(mask):
+    """(kind, seg array or None, parent array or None, window) of a mask."""
+    if isinstance(mask, Causal):
+        return CAUSAL, None, None, mask.window
+    if isinstance(mask, Full):
+        return FULL, None, None, 0
+    if isinstance(mask, Tree):
+        return (TREE, np.ascontiguousarray(mask.seg, dtype=np.int32),
+                np.ascontiguousarray(mask.parent, dtype=np.int32), mask.window)
+    raise TypeError("unknown mask %r" % (mask,))
+
+
+def attention_backward(Q, K, V, qpos, kpos, O, L, G, mask=Causal(), scale: Optional[float] = None, rows=None):
+    """Gradients (dQ [H, n_rows, d], dK [H, nk, d], dV [H, nk, dv]) of
+    attention over the keys of this call, given the rows' complete outputs
+    O [H, n_rows, dv] and LSE L [H, n_rows] (over all their visible keys) and
+    the output gradient G ("Context Parallelism in ART", section 04).
+    Summing over any partition of the keys gives the full gradients."""
+    lib = _load()
+    q, dt = _as_array(Q)
+    k, dk_ = _as_array(K)
+    v, dv_ = _as_array(V)
+    if not (dt == dk_ == dv_):
+        raise TypeError("Q, K and V must share one dtype")
+    H, nq, d = q.shape
+    nk = k.shape[1]
+    dv = v.shape[2]
+    qpos = np.ascontiguousarray(qpos, dtype=np.int64)
+    kpos = np.ascontiguousarray(kpos, dtype=np.int64)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n_rows = nq if rows_arr is None else rows_arr.shape[0]
+    O = np.ascontiguousarray(O, dtype=np.float64)
+    L = np.ascontiguousarray(L, dtype=np.float64)
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    if O.shape != (H, n_rows, dv) or G.shape != O.shape or L.shape != (H, n_rows):
+        raise ValueError("O, G must be [H, n_rows, dv] and L [H, n_rows]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    kind, seg, par, window = _mask_fields(mask)
+    dQ = np.zeros((H, n_rows, d))
+    dK = np.zeros((H, nk, d))
+    dV = np.zeros((H, nk, dv))
+    rc = lib.oracle_attention_backward(
+        H, nq, nk, d, dv, dt, q.ctypes.data, nq * d, d, k.ctypes.data, nk * d, d, v.ctypes.data, nk * dv, dv,
+        qpos.ctypes.data, kpos.ctypes.data, kind, None if seg is None else seg.ctypes.data,
+        0 if seg is None else seg.shape[0], None if par is None else par.ctypes.data,
+        0 if par is None else par.shape[0], int(window), float(scale),
+        None if rows_arr is None else rows_arr.ctypes.data, n_rows,
+        O.ctypes.data, L.ctypes.data, G.ctypes.data, dQ.ctypes.data, dK.ctypes.data, dV.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_attention_backward rejected its arguments")
+    return dQ, dK, dV
+
+
+def merge_backward(parts, O, L, G, gL=None):
+    """Adjoints [(dO_r, dL_r)] of the merge of ``parts`` = [(O_r, L_r)] into
+    (O, L), for output gradient G and optional LSE gradient gL ("Context
+    Parallelism in ART", section 04)."""
+    lib = _load()
+    parts = [(np.ascontiguousarray(o, dtype=np.float64), np.ascontiguousarray(l, dtype=np.float64))
+             for o, l in parts]
+    O = np.ascontiguousarray(O, dtype=np.float64)
+    L = np.ascontiguousarray(L, dtype=np.float64)
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    dv = O.shape[-1]
+    n_rows = L.size
+    gl = None if gL is None else np.ascontiguousarray(gL, dtype=np.float64)
+    outs = [(np.zeros_like(o), np.zeros_like(l)) for o, l in parts]
+    n = len(parts)
+    P = ctypes.c_void_p
+    op = (P * n)(*[o.ctypes.data for o, _ in parts])
+    lp = (P * n)(*[l.ctypes.data for _, l in parts])
+    dop = (P * n)(*[o.ctypes.data for o, _ in outs])
+    dlp = (P * n)(*[l.ctypes.data for _, l in outs])
+    lib.oracle_merge_backward(n, op, lp, n_rows, dv, O.ctypes.data, L.ctypes.data, G.ctypes.data,
+                              None if gl is None else gl.ctypes.data, dop, dlp)
+    return outs
+
+
+def sink_backward(O, L, a, G):
+    """Adjoints (dO, dL, da) of the sink step y = w O, w = exp(L -
+    logaddexp(L, a)) for output gradient G ("Context Parallelism in ART",
+    section 06).  O is the output before the sink."""
+    lib = _load()
+    O = np.ascontiguousarray(O, dtype=np.float64)
+    L = np.ascontiguousarray(L, dtype=np.float64)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    H, n, dv = O.shape
+    dO = np.zeros_like(O)
+    dL = np.zeros_like(L)
+    da = np.zeros_like(a)
+    lib.oracle_sink_backward(H, n, dv, O.ctypes.data, L.ctypes.data, a.ctypes.data, G.ctypes.data,
+                             dO.ctypes.data, dL.ctypes.data, da.ctypes.data)
+    return dO, dL, da

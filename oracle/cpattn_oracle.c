@@ -30,6 +30,10 @@
  *  - The learned attention sink, applied once to a complete result (same
  *    page, section 06): oracle_apply_sink.
  *
+ *  - Backward: attention gradients with the global softmax derivative
+ *    (section 04), the merge adjoints (section 04) and the sink adjoints
+ *    (section 06).
+ *
  *  Readings where the pages are silent (each is also listed in the design doc):
  *  a query with no visible key gives O = 0 and L = -inf; merging with such a
  *  partial leaves the other side unchanged; merging two empty partials gives
@@ -206,6 +210,140 @@ int oracle_attention(int64_t H, int64_t nq, int64_t nk, int64_t d, int64_t dv, i
     }
     free(lp);
     return 0;
+}
+
+/*
+ * oracle_attention_backward: gradients of attention of the selected query
+ * rows, given each row's complete output O and log-sum-exp L (over all of its
+ * visible keys, not only this call's) and the incoming output gradient G
+ * ("Context Parallelism in ART", section 04, the global softmax derivative):
+ * with p_j = exp(s_j - L) over the keys of this call that the row sees and
+ * D = dot(G, O),
+ *     dS_j = p_j (dot(G, v_j) - D),   dV_j += p_j G,
+ *     dQ   += scale dS_j k_j,          dK_j += scale dS_j q.
+ * Because p_j and D are global, summing the calls over any partition of the
+ * keys gives the gradients of the unpartitioned attention.
+ *   O, G, dQ: [H][n_rows][d or dv] for the selected rows; L: [H][n_rows];
+ *   dK: [H][nk][d], dV: [H][nk][dv].  All fp64, accumulated into (the caller
+ *   zeroes them).  Rows are processed one after another (dK and dV are
+ *   shared).  Returns 0, or -1 on a bad argument.
+ */
+int oracle_attention_backward(int64_t H, int64_t nq, int64_t nk, int64_t d, int64_t dv, int dtype,
+                              const void* Q, int64_t q_sh, int64_t q_st,
+                              const void* K, int64_t k_sh, int64_t k_st,
+                              const void* V, int64_t v_sh, int64_t v_st,
+                              const int64_t* qpos, const int64_t* kpos,
+                              int kind, const int32_t* seg, int64_t n_pos,
+                              const int32_t* parent, int32_t n_seg,
+                              int64_t window, double scale, const int64_t* rows, int64_t n_rows,
+                              const double* O, const double* L, const double* G,
+                              double* dQ, double* dK, double* dV) {
+    if (H < 0 || nq < 0 || nk < 0 || d <= 0 || dv <= 0 || window < 0) return -1;
+    if (window > 0 && kind == OR_FULL) return -1;
+    if (!rows) n_rows = nq;
+    if (kind == OR_TREE) {
+        for (int64_t j = 0; j < nk; ++j)
+            if (kpos[j] < 0 || kpos[j] >= n_pos) return -1;
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t i = rows ? rows[r] : r;
+            if (i < 0 || i >= nq || qpos[i] < 0 || qpos[i] >= n_pos) return -1;
+        }
+    }
+    int64_t* lp = NULL;
+    if (window > 0 && kind == OR_TREE) {
+        lp = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_pos > 0 ? n_pos : 1));
+        if (!lp || logical_positions(seg, n_pos, parent, n_seg, lp) != 0) { free(lp); return -1; }
+    }
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t i = rows ? rows[r] : r;
+            const double* o = O + (h * n_rows + r) * dv;
+            const double* g = G + (h * n_rows + r) * dv;
+            double* dq = dQ + (h * n_rows + r) * d;
+            double l = L[h * n_rows + r];
+            if (l == -INFINITY) continue;   /* the row saw no key at all: no gradient */
+            double D = 0.0;
+            for (int64_t c = 0; c < dv; ++c) D += g[c] * o[c];
+            for (int64_t j = 0; j < nk; ++j) {
+                if (!visible(kind, seg, parent, n_seg, qpos[i], kpos[j])) continue;
+                if (window > 0) {
+                    int64_t lq = lp ? lp[qpos[i]] : qpos[i], lk = lp ? lp[kpos[j]] : kpos[j];
+                    if (lq - lk >= window) continue;
+                }
+                double s = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    s += widen(Q, dtype, h * q_sh + i * q_st + c) * widen(K, dtype, h * k_sh + j * k_st + c);
+                double p = exp(s * scale - l);
+                double gv = 0.0;
+                for (int64_t c = 0; c < dv; ++c) gv += g[c] * widen(V, dtype, h * v_sh + j * v_st + c);
+                double ds = p * (gv - D);
+                for (int64_t c = 0; c < dv; ++c) dV[(h * nk + j) * dv + c] += p * g[c];
+                for (int64_t c = 0; c < d; ++c) {
+                    dq[c] += scale * ds * widen(K, dtype, h * k_sh + j * k_st + c);
+                    dK[(h * nk + j) * d + c] += scale * ds * widen(Q, dtype, h * q_sh + i * q_st + c);
+                }
+            }
+        }
+    }
+    free(lp);
+    return 0;
+}
+
+/*
+ * oracle_merge2_backward: adjoints of the two-way merge (same page, section
+ * 04): with w_r = exp(L_r - L) for the merged (O, L), an incoming output
+ * gradient G and LSE gradient gL,
+ *     dO_r = w_r G,    dL_r = w_r (dot(G, o_r - o) + gL).
+ * (The gL term is the derivative of L = log sum exp(L_r), i.e. w_r.)  Rows
+ * whose merged L is -inf get zero adjoints.  All [n_rows][dv] / [n_rows].
+ */
+void oracle_merge_backward(int n_parts, const double* const* O_parts, const double* const* L_parts,
+                           int64_t n_rows, int64_t dv, const double* O, const double* L,
+                           const double* G, const double* gL, double* const* dO_parts, double* const* dL_parts) {
+    for (int p = 0; p < n_parts; ++p) {
+        for (int64_t r = 0; r < n_rows; ++r) {
+            const double* o_r = O_parts[p] + r * dv;
+            const double* o = O + r * dv;
+            const double* g = G + r * dv;
+            double w = (L[r] == -INFINITY || L_parts[p][r] == -INFINITY) ? 0.0 : exp(L_parts[p][r] - L[r]);
+            double dot = 0.0;
+            for (int64_t c = 0; c < dv; ++c) {
+                dO_parts[p][r * dv + c] = w * g[c];
+                dot += g[c] * (o_r[c] - o[c]);
+            }
+            dL_parts[p][r] = w * (dot + (gL ? gL[r] : 0.0));
+        }
+    }
+}
+
+/*
+ * oracle_sink_backward: adjoints of the sink step (same page, section 06):
+ * y = w o with w = exp(L - L_total), L_total = logaddexp(L, a); for an
+ * incoming gradient g of y,
+ *     dJ/do = w g,   dJ/dL = w (1 - w) dot(g, o),   dJ/da = -w (1 - w) dot(g, o)
+ * summed over the rows of each head for a.  O is the output before the sink.
+ * O, G, dO: [H][n_rows][dv]; L, dL: [H][n_rows]; a, da: [H].
+ */
+void oracle_sink_backward(int64_t n_heads, int64_t n_rows, int64_t dv, const double* O, const double* L,
+                          const double* a, const double* G, double* dO, double* dL, double* da) {
+    for (int64_t h = 0; h < n_heads; ++h) {
+        da[h] = 0.0;
+        for (int64_t r = 0; r < n_rows; ++r) {
+            double l = L[h * n_rows + r];
+            double m = l > a[h] ? l : a[h];
+            double lt = (m == -INFINITY) ? -INFINITY : m + log(exp(l - m) + exp(a[h] - m));
+            double w = (l == -INFINITY) ? 0.0 : exp(l - lt);
+            const double* o = O + (h * n_rows + r) * dv;
+            const double* g = G + (h * n_rows + r) * dv;
+            double dot = 0.0;
+            for (int64_t c = 0; c < dv; ++c) {
+                dO[(h * n_rows + r) * dv + c] = w * g[c];
+                dot += g[c] * o[c];
+            }
+            dL[h * n_rows + r] = w * (1.0 - w) * dot;
+            da[h] += -w * (1.0 - w) * dot;
+        }
+    }
 }
 
 /*

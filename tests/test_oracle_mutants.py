@@ -26,6 +26,12 @@ MUTANTS = {
     "window_off_by_one": ("if (lq - lk >= window) continue;", "if (lq - lk > window) continue;"),
     "window_on_storage_positions": ("int64_t lq = lp ? lp[qpos[i]] : qpos[i], lk = lp ? lp[kpos[j]] : kpos[j];",
                                     "int64_t lq = qpos[i], lk = kpos[j];"),
+    "backward_drops_D": ("double ds = p * (gv - D);", "double ds = p * gv;"),
+    "backward_dk_from_k": ("dK[(h * nk + j) * d + c] += scale * ds * widen(Q, dtype, h * q_sh + i * q_st + c);",
+                           "dK[(h * nk + j) * d + c] += scale * ds * widen(K, dtype, h * k_sh + j * k_st + c);"),
+    "merge_adjoint_drops_lse_term": ("dL_parts[p][r] = w * (dot + (gL ? gL[r] : 0.0));",
+                                     "dL_parts[p][r] = w * dot;"),
+    "sink_adjoint_sign": ("da[h] += -w * (1.0 - w) * dot;", "da[h] += w * (1.0 - w) * dot;"),
     "sink_weight_inverted": ("double w = (l == -INFINITY) ? 0.0 : exp(l - lt);",
                              "double w = (l == -INFINITY) ? 0.0 : exp(lt - l);"),
     "sink_mass_dropped": ("m + log(exp(l - m) + exp(a[h] - m));", "m + log(exp(l - m));"),

@@ -584,3 +584,117 @@ def test_window_covering_everything_is_no_window():
     a = oracle.attention(Q, K, V, pos, pos, oracle.Tree(seg, parent))
     b = oracle.attention(Q, K, V, pos, pos, oracle.Tree(seg, parent, window=n))
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------
+# backward ("Context Parallelism in ART", section 04: the global softmax
+# derivative and the merge adjoints; section 06: the sink adjoints)
+# ----------------------------------------------------------------------------
+def _fd(f, X, eps=1e-6):
+    """Central finite differences of the scalar f at X (all entries)."""
+    g = np.zeros_like(X)
+    for idx in np.ndindex(X.shape):
+        Xp = X.copy()
+        Xp[idx] += eps
+        Xm = X.copy()
+        Xm[idx] -= eps
+        g[idx] = (f(Xp) - f(Xm)) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("maskname", ["causal", "tree", "full", "tree_window"])
+def test_attention_backward_vs_finite_differences(maskname):
+    rng = np.random.default_rng(31)
+    H, d = 2, 4
+    if maskname.startswith("tree"):
+        seg, parent = _random_tree(rng, 4, 1, 4)
+        n = len(seg)
+        mask = oracle.Tree(seg, parent, window=3 if maskname == "tree_window" else 0)
+    else:
+        n = 10
+        mask = oracle.Causal() if maskname == "causal" else oracle.Full()
+    Q, K, V, G = (_rand(rng, H, n, d) for _ in range(4))
+    pos = np.arange(n)
+
+    def J(Q_, K_, V_):
+        O, L = oracle.attention(Q_, K_, V_, pos, pos, mask, 0.7)
+        return float((O * G).sum())
+
+    O, L = oracle.attention(Q, K, V, pos, pos, mask, 0.7)
+    dQ, dK, dV = oracle.attention_backward(Q, K, V, pos, pos, O, L, G, mask, 0.7)
+    assert np.abs(dQ - _fd(lambda X: J(X, K, V), Q)).max() <= 1e-7
+    assert np.abs(dK - _fd(lambda X: J(Q, X, V), K)).max() <= 1e-7
+    assert np.abs(dV - _fd(lambda X: J(Q, K, X), V)).max() <= 1e-7
+
+
+def test_staged_backward_with_global_softmax_sums_to_full():
+    """Every stage uses the complete O and LSE: the stages' dQ add up and
+    each key block gets exactly its share of dK, dV."""
+    rng = np.random.default_rng(32)
+    H, n, d, N = 2, 48, 8, 4
+    Q, K, V, G = (_rand(rng, H, n, d) for _ in range(4))
+    pos = np.arange(n)
+    O, L = oracle.attention(Q, K, V, pos, pos, oracle.Causal())
+    dQ, dK, dV = oracle.attention_backward(Q, K, V, pos, pos, O, L, G, oracle.Causal())
+    dQs = np.zeros_like(dQ)
+    for b in workloads.zigzag(n, N):
+        q_, k_, v_ = oracle.attention_backward(Q, K[:, b], V[:, b], pos, pos[b], O, L, G, oracle.Causal())
+        dQs += q_
+        assert np.abs(k_ - dK[:, b]).max() <= 1e-12 and np.abs(v_ - dV[:, b]).max() <= 1e-12
+    assert np.abs(dQs - dQ).max() <= 1e-12
+
+
+def test_local_denominators_are_wrong():
+    """The page's warning: running each stage's softmax backward with its own
+    (local) O and LSE and the original output gradient is not the gradient."""
+    rng = np.random.default_rng(33)
+    H, n, d, N = 1, 32, 8, 2
+    Q, K, V, G = (_rand(rng, H, n, d) for _ in range(4))
+    pos = np.arange(n)
+    O, L = oracle.attention(Q, K, V, pos, pos, oracle.Full())
+    dQ, _, _ = oracle.attention_backward(Q, K, V, pos, pos, O, L, G, oracle.Full())
+    wrong = np.zeros_like(dQ)
+    for b in workloads.contiguous(n, N):
+        Ol, Ll = oracle.attention(Q, K[:, b], V[:, b], pos, pos[b], oracle.Full())
+        wrong += oracle.attention_backward(Q, K[:, b], V[:, b], pos, pos[b], Ol, Ll, G, oracle.Full())[0]
+    assert np.abs(wrong - dQ).max() > 1e-2
+
+
+def test_merge_backward_vs_finite_differences():
+    rng = np.random.default_rng(34)
+    rows, dv, n_parts = 5, 3, 3
+    parts = [(_rand(rng, rows, dv), 2 * _rand(rng, rows)) for _ in range(n_parts)]
+    parts[1][1][2] = -np.inf
+    parts[1][0][2] = 0.0
+    G, gL = _rand(rng, rows, dv), _rand(rng, rows)
+
+    def J(ps):
+        O, L = oracle.merge(ps)
+        return float((O * G).sum() + (L * gL).sum())
+
+    O, L = oracle.merge(parts)
+    adj = oracle.merge_backward(parts, O, L, G, gL)
+    for p in range(n_parts):
+        fo = _fd(lambda X: J([(X if i == p else parts[i][0], parts[i][1]) for i in range(n_parts)]), parts[p][0])
+        L_p = parts[p][1].copy()
+        fin = np.isfinite(L_p)
+        L_p[~fin] = 0.0   # the empty row carries no mass: perturb only finite entries
+        fl = _fd(lambda X: J([(parts[i][0], np.where(fin, X, -np.inf) if i == p else parts[i][1])
+                              for i in range(n_parts)]), L_p)
+        assert np.abs(adj[p][0] - fo).max() <= 1e-7
+        assert np.abs(adj[p][1][fin] - fl[fin]).max() <= 1e-7
+
+
+def test_sink_backward_vs_finite_differences():
+    rng = np.random.default_rng(35)
+    H, n, dv = 2, 4, 3
+    O, L, a, G = _rand(rng, H, n, dv), 2 * _rand(rng, H, n), _rand(rng, H), _rand(rng, H, n, dv)
+
+    def J(O_, L_, a_):
+        y, _ = oracle.apply_sink(O_, L_, a_)
+        return float((y * G).sum())
+
+    dO, dL, da = oracle.sink_backward(O, L, a, G)
+    assert np.abs(dO - _fd(lambda X: J(X, L, a), O)).max() <= 1e-7
+    assert np.abs(dL - _fd(lambda X: J(O, X, a), L)).max() <= 1e-7
+    assert np.abs(da - _fd(lambda X: J(O, L, X), a)).max() <= 1e-7
