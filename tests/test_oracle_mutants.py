@@ -19,8 +19,8 @@ MUTANTS = {
     "merge_weight_sign": ("double a = exp(la - m), b = exp(lb - m);",
                           "double a = exp(m - la), b = exp(m - lb);"),
     "lse_drops_max": ("double lse = m + log(z);", "double lse = log(z);"),
-    "key_operand_swapped": ("widen(K, dtype, h * k_sh + j * k_st + c)",
-                            "widen(V, dtype, h * v_sh + j * v_st + c)"),
+    "key_operand_swapped": ("                           widen(K, dtype, h * k_sh + j * k_st + c);",
+                            "                           widen(V, dtype, h * v_sh + j * v_st + c);"),
     "scale_dropped": ("s[a] = acc * scale;", "s[a] = acc;"),
     "output_unnormalised": ("double p = exp(s[a] - lse);", "double p = exp(s[a] - m);"),
     "window_off_by_one": ("if (lq - lk >= window) continue;", "if (lq - lk > window) continue;"),
@@ -32,9 +32,10 @@ MUTANTS = {
     "merge_adjoint_drops_lse_term": ("dL_parts[p][r] = w * (dot + (gL ? gL[r] : 0.0));",
                                      "dL_parts[p][r] = w * dot;"),
     "sink_adjoint_sign": ("da[h] += -w * (1.0 - w) * dot;", "da[h] += w * (1.0 - w) * dot;"),
-    "sink_weight_inverted": ("double w = (l == -INFINITY) ? 0.0 : exp(l - lt);",
-                             "double w = (l == -INFINITY) ? 0.0 : exp(lt - l);"),
-    "sink_mass_dropped": ("m + log(exp(l - m) + exp(a[h] - m));", "m + log(exp(l - m));"),
+    "sink_weight_inverted": ("double w = (l == -INFINITY) ? 0.0 : exp(l - lt);\n            double* o",
+                             "double w = (l == -INFINITY) ? 0.0 : exp(lt - l);\n            double* o"),
+    "sink_mass_dropped": ("m + log(exp(l - m) + exp(a[h] - m));\n            double w = (l == -INFINITY) ? 0.0 : exp(l - lt);\n            double* o",
+                          "m + log(exp(l - m));\n            double w = (l == -INFINITY) ? 0.0 : exp(l - lt);\n            double* o"),
 }
 
 
@@ -42,7 +43,8 @@ MUTANTS = {
 def test_pins_catch_planted_mistake(name, tmp_path):
     before, after = MUTANTS[name]
     text = open(SRC).read()
-    assert text.count(before) == 1, "mutation site not found: %s" % name
+    # a rule written in several places (forward and backward) is mutated everywhere
+    assert text.count(before) >= 1, "mutation site not found: %s" % name
     mutated = tmp_path / "mutant.c"
     mutated.write_text(text.replace(before, after))
     lib = tmp_path / "libmutant.so"
