@@ -233,6 +233,46 @@ def window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N, window: i
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def backward_ring(cp, torch, dev, qd, kd, vd, seg, parent, N, outs, A, steps: int = 5):
+    """Backward of the headline ring (global softmax derivative): per step one
+    D = dot(dO, O) pass per rank and, per ring round, a dQ launch and a dK/dV
+    launch.  FLOPs counted as 2.5x the forward's on visible pairs (10 d per
+    pair and head: the recomputed QK^T plus the dP, dV, dQ and dK products)."""
+    H, n, d = qd.shape
+    c = n // N
+    g = torch.Generator(device="cpu").manual_seed(7)
+    gd = torch.randn((H, n, d), generator=g).to(torch.bfloat16).to(dev)
+    mask = cp.Mask.tree(seg, parent)
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    pos = [(r * c, 1) for r in range(N)]
+    douts = [x.contiguous() for x in blk(gd)]
+    deltas = [torch.empty((H, c), dtype=torch.float32, device=dev) for _ in range(N)]
+    grads = [tuple(torch.zeros((H, c, d), dtype=torch.float32, device=dev) for _ in range(3)) for _ in range(N)]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for r in range(N):
+            cp.backward_delta(outs[r][0], douts[r], deltas[r], stream=stream)
+        cp.ring_backward(blk(qd), blk(kd), blk(vd), pos, mask, [outs[r][1] for r in range(N)], deltas, douts,
+                         grads=grads, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    mask.free()
+    flops = 10.0 * d * H * A
+    return {"workload": "tree64k ring of %d, backward (dQ, dK, dV) with the complete O and LSE" % N,
+            "ms_per_step": round(ms, 4), "flops_convention": "10 d per visible pair and head (2.5x forward)",
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +436,7 @@ def main():
         result["load_balance"] = load_balance(cp, workloads, torch, dev)
         result["gqa"] = gqa_ring(cp, workloads, torch, dev, seg, parent, N, flops)
         result["window"] = window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N)
+        result["backward"] = backward_ring(cp, torch, dev, qd, kd, vd, seg, parent, N, outs, A)
 
     if not args.no_cpu:
         import oracle

@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
 * :func:`ring_plan` -- per-rank, per-round visible-pair counts (host only).
 * :func:`apply_sink` -- learned attention-sink logits applied once to a
   complete result.
+* :func:`backward_delta`, :func:`partial_backward`, :func:`ring_backward` --
+  gradients with the global softmax derivative.
 """
 from __future__ import annotations
 
@@ -81,9 +83,15 @@ def lib():
                                                  ctypes.c_float, P, P, P]
         L.cpattn_ring_plan.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P]
         L.cpattn_apply_sink.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
+        L.cpattn_backward_delta.argtypes = [P, ctypes.POINTER(_Tensor), P, P]
+        L.cpattn_partial_backward.argtypes = [ctypes.POINTER(_Tensor)] * 3 + [P, _PosMap, _PosMap, ctypes.c_float,
+                                                                               P, P, ctypes.POINTER(_Tensor), P, P, P,
+                                                                               P]
+        L.cpattn_ring_backward.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P]
         for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
                   "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan",
-                  "cpattn_apply_sink", "cpattn_mask_with_window"):
+                  "cpattn_apply_sink", "cpattn_mask_with_window", "cpattn_backward_delta",
+                  "cpattn_partial_backward", "cpattn_ring_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -355,3 +363,74 @@ def apply_sink(o: torch.Tensor, lse: torch.Tensor, sink_logits: torch.Tensor, st
     _check(lib().cpattn_apply_sink(o.data_ptr(), lse.data_ptr(), sink_logits.data_ptr(), H, n, d,
                                    _stream(stream)))
     return o, lse
+
+
+def _f32_dev(t, name):
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous fp32 device tensor" % name)
+    return t.data_ptr()
+
+
+def backward_delta(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None, stream=None):
+    """D = rowsum(dO * O) per query row ([H, n]) from the complete output O
+    (fp32 [H, n, d]) and the output gradient dout (bf16 or fp32)."""
+    H, n, d = dout.shape
+    if o.shape != (H, n, d):
+        raise ValueError("o and dout shapes differ")
+    if delta is None:
+        delta = torch.empty((H, n), dtype=torch.float32, device=dout.device)
+    dd = _desc(dout, "dout")
+    _check(lib().cpattn_backward_delta(_f32_dev(o, "o"), ctypes.byref(dd), _f32_dev(delta, "delta"),
+                                       _stream(stream)))
+    return delta
+
+
+def partial_backward(q, k, v, mask: Mask, lse, delta, dout, q_pos=(0, 1), k_pos=(0, 1), scale=None, grads=None,
+                     stream=None):
+    """Adds this (query block, K/V block) pair's gradients into ``grads`` =
+    (dq [H, n_q, d], dk [H_kv, n_k, d], dv [H_kv, n_k, d]) fp32 (zero-filled
+    new tensors if None), using the queries' complete ``lse`` and ``delta``."""
+    H, nq, d = q.shape
+    Hk, nk, _ = k.shape
+    if grads is None:
+        grads = (torch.zeros((H, nq, d), dtype=torch.float32, device=q.device),
+                 torch.zeros((Hk, nk, d), dtype=torch.float32, device=q.device),
+                 torch.zeros((Hk, nk, d), dtype=torch.float32, device=q.device))
+    dq, dk, dv = grads
+    qd, kd, vd, dd = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(dout, "dout")
+    _check(lib().cpattn_partial_backward(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), mask.handle,
+                                         _posmap(q_pos), _posmap(k_pos),
+                                         float(_default_scale(d) if scale is None else scale),
+                                         _f32_dev(lse, "lse"), _f32_dev(delta, "delta"), ctypes.byref(dd),
+                                         _f32_dev(dq, "dq"), _f32_dev(dk, "dk"), _f32_dev(dv, "dv"),
+                                         _stream(stream)))
+    return grads
+
+
+def ring_backward(q_blocks, k_blocks, v_blocks, pos, mask: Mask, lses, deltas, douts, scale=None, grads=None,
+                  stream=None):
+    """Backward of the ring of N ranks: in round k rank r's queries meet the
+    keys of rank (r - k) mod N; dQ stays with rank r, dK and dV are added to
+    the key owner's buffers.  ``grads[r]`` = (dq, dk, dv) fp32 per rank
+    (zero-filled new tensors if None); returns it."""
+    N = len(k_blocks)
+    d = q_blocks[0].shape[2]
+    if grads is None:
+        grads = [(torch.zeros(q_blocks[r].shape, dtype=torch.float32, device=q_blocks[r].device),
+                  torch.zeros(k_blocks[r].shape, dtype=torch.float32, device=k_blocks[r].device),
+                  torch.zeros(v_blocks[r].shape, dtype=torch.float32, device=v_blocks[r].device)) for r in range(N)]
+    qd = (_Tensor * N)(*[_desc(t, "q") for t in q_blocks])
+    kd = (_Tensor * N)(*[_desc(t, "k") for t in k_blocks])
+    vd = (_Tensor * N)(*[_desc(t, "v") for t in v_blocks])
+    od = (_Tensor * N)(*[_desc(t, "dout") for t in douts])
+    pd = (_PosMap * N)(*[_posmap(p) for p in pos])
+    P = ctypes.c_void_p
+    lp = (P * N)(*[_f32_dev(t, "lse") for t in lses])
+    dp = (P * N)(*[_f32_dev(t, "delta") for t in deltas])
+    gq = (P * N)(*[_f32_dev(g[0], "dq") for g in grads])
+    gk = (P * N)(*[_f32_dev(g[1], "dk") for g in grads])
+    gv = (P * N)(*[_f32_dev(g[2], "dv") for g in grads])
+    _check(lib().cpattn_ring_backward(N, qd, kd, vd, pd, mask.handle,
+                                      float(_default_scale(d) if scale is None else scale), lp, dp, od, gq, gk, gv,
+                                      _stream(stream)))
+    return grads

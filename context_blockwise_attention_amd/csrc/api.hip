@@ -17,6 +17,7 @@
 
 #include "../../include/cpattn.h"
 #include "attn_bf16_kernel.hpp"
+#include "attn_bwd_kernel.hpp"
 #include "attn_kernel.hpp"
 #include "merge_kernel.hpp"
 
@@ -753,4 +754,195 @@ extern "C" int cpattn_apply_sink(float* o, float* lse, const float* sink_logits,
     hipLaunchKernelGGL(sink_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? CPATTN_OK : hip_fail(e, "sink launch");
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static int launch_bwd_t(BwdArgs& a, bool dkv, hipStream_t st) {
+    using S = BwdStage<T, D>;
+    const int smem_dq = (2 * S::ROW_ELEMS + S::T_ELEMS) * (int)sizeof(T) + kBwdTile * 4;
+    const int smem_dkv = (2 * S::ROW_ELEMS + 2 * S::T_ELEMS) * (int)sizeof(T) + 2 * kBwdTile * 4;
+    const auto kq = attn_bwd_dq_kernel<T, D>;
+    const auto kkv = attn_bwd_dkv_kernel<T, D>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kq),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem_dq);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kkv), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    smem_dkv);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        attr_set = true;
+    }
+    if (a.total_wg == 0) return CPATTN_OK;
+    if (dkv) hipLaunchKernelGGL(kkv, dim3(a.total_wg), dim3(kBwdThreads), smem_dkv, st, a);
+    else hipLaunchKernelGGL(kq, dim3(a.total_wg), dim3(kBwdThreads), smem_dq, st, a);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "backward launch");
+}
+
+static int launch_bwd(BwdArgs& a, bool dkv, int dtype, int d, hipStream_t st) {
+    if (dtype == CPATTN_BF16) return d == 128 ? launch_bwd_t<__bf16, 128>(a, dkv, st) : launch_bwd_t<__bf16, 64>(a, dkv, st);
+    return d == 128 ? launch_bwd_t<float, 128>(a, dkv, st) : launch_bwd_t<float, 64>(a, dkv, st);
+}
+
+struct BwdPair {
+    const cpattn_tensor *q, *k, *v, *dout;
+    cpattn_posmap qp, kp;
+    const float *lse, *delta;
+    float *dq, *dk, *dv;
+};
+
+// One dQ launch and one dK/dV launch for a set of pairs; the pairs of one
+// call must not share a query block (dQ) or a key block (dK/dV).
+static int run_bwd(const std::vector<BwdPair>& pairs, const cpattn_mask* m, float scale, hipStream_t st) {
+    for (size_t first = 0; first < pairs.size(); first += kMaxJobs) {
+        const size_t n = std::min<size_t>(kMaxJobs, pairs.size() - first);
+        for (int dkv = 0; dkv < 2; ++dkv) {
+            BwdArgs a{};
+            a.mask = mask_args(m);
+            a.scale = scale;
+            a.scale_log2 = scale * 1.4426950408889634f;
+            a.n_jobs = (int32_t)n;
+            int64_t wg = 0;
+            int dtype = 0, d = 0;
+            for (size_t i = 0; i < n; ++i) {
+                const BwdPair& P = pairs[first + i];
+                BwdJob& j = a.jobs[i];
+                j.q = P.q->data;
+                j.k = P.k->data;
+                j.v = P.v->data;
+                j.dout = P.dout->data;
+                j.lse = P.lse;
+                j.delta = P.delta;
+                j.dq = P.dq;
+                j.dk = P.dk;
+                j.dv = P.dv;
+                j.q_sh = P.q->stride_head;
+                j.k_sh = P.k->stride_head;
+                j.v_sh = P.v->stride_head;
+                j.do_sh = P.dout->stride_head;
+                j.q_st = (int32_t)P.q->stride_tok;
+                j.k_st = (int32_t)P.k->stride_tok;
+                j.v_st = (int32_t)P.v->stride_tok;
+                j.do_st = (int32_t)P.dout->stride_tok;
+                j.qbase = (int32_t)P.qp.base;
+                j.qstride = (int32_t)P.qp.stride;
+                j.kbase = (int32_t)P.kp.base;
+                j.kstride = (int32_t)P.kp.stride;
+                j.n_q = (int32_t)P.q->n_tok;
+                j.n_k = (int32_t)P.k->n_tok;
+                j.kv_group = (int32_t)(P.q->n_heads / P.k->n_heads);
+                const int64_t rows = dkv ? P.k->n_tok : P.q->n_tok;
+                j.tiles = (int32_t)((rows + kBwdRows - 1) / kBwdRows);
+                a.heads = (int32_t)(dkv ? P.k->n_heads : P.q->n_heads);
+                wg += (int64_t)a.heads * j.tiles;
+                dtype = P.q->dtype;
+                d = (int)P.q->d;
+            }
+            if (wg > INT32_MAX / 2) return fail(CPATTN_EUNSUPPORTED, "too many workgroups in one launch");
+            a.total_wg = (int32_t)wg;
+            int rc = launch_bwd(a, dkv == 1, dtype, d, st);
+            if (rc != CPATTN_OK) return rc;
+        }
+    }
+    return CPATTN_OK;
+}
+
+static int check_bwd_common(const cpattn_tensor* q, const cpattn_tensor* dout, const cpattn_mask* mask,
+                            const float* lse, const float* delta, const char* who) {
+    int rc;
+    if (!mask) return fail(CPATTN_EINVAL, "%s: mask is NULL", who);
+    if (mask->window > 0) return fail(CPATTN_EUNSUPPORTED, "%s: the backward does not support sliding windows", who);
+    if ((rc = check_tensor(dout, who, "dout"))) return rc;
+    if (dout->dtype != q->dtype || dout->d != q->d || dout->n_heads != q->n_heads || dout->n_tok != q->n_tok)
+        return fail(CPATTN_EINVAL, "%s: dout must match q in dtype, heads, tokens and head dim", who);
+    if (q->n_tok > 0 && (!lse || !delta)) return fail(CPATTN_EINVAL, "%s: lse or delta is NULL", who);
+    return CPATTN_OK;
+}
+
+extern "C" int cpattn_backward_delta(const float* o, const cpattn_tensor* dout, float* delta, void* stream) {
+    const char* who = "cpattn_backward_delta";
+    int rc;
+    if ((rc = check_tensor(dout, who, "dout"))) return rc;
+    if (dout->n_tok == 0) return CPATTN_OK;
+    if (!o || !delta) return fail(CPATTN_EINVAL, "%s: NULL pointer", who);
+    const int64_t rows = dout->n_heads * dout->n_tok;
+    const int64_t blocks = (rows + 3) / 4;
+    if (blocks > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many rows", who);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dout->dtype == CPATTN_BF16)
+        hipLaunchKernelGGL(bwd_delta_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, st, o,
+                           reinterpret_cast<const __bf16*>(dout->data), dout->stride_head, (int32_t)dout->stride_tok,
+                           delta, rows, (int32_t)dout->n_tok, (int32_t)dout->d);
+    else
+        hipLaunchKernelGGL(bwd_delta_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, o,
+                           reinterpret_cast<const float*>(dout->data), dout->stride_head, (int32_t)dout->stride_tok,
+                           delta, rows, (int32_t)dout->n_tok, (int32_t)dout->d);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "delta launch");
+}
+
+extern "C" int cpattn_partial_backward(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                       const cpattn_mask* mask, cpattn_posmap q_pos, cpattn_posmap k_pos, float scale,
+                                       const float* lse, const float* delta, const cpattn_tensor* dout, float* dq,
+                                       float* dk, float* dv, void* stream) {
+    const char* who = "cpattn_partial_backward";
+    int rc;
+    if ((rc = check_qkv(q, k, v, who))) return rc;
+    if ((rc = check_scale(scale, who))) return rc;
+    if ((rc = check_bwd_common(q, dout, mask, lse, delta, who))) return rc;
+    if (q->n_tok == 0 || k->n_tok == 0) return CPATTN_OK;
+    if ((rc = check_out(dq, lse, who)) || (rc = check_out(dk, delta, who)) || (rc = check_out(dv, delta, who))) return rc;
+    if ((rc = check_posmap(q_pos, q->n_tok, mask, who, "q_pos")) || (rc = check_posmap(k_pos, k->n_tok, mask, who, "k_pos")))
+        return rc;
+    if (!pair_nonempty(mask, q_pos, q->n_tok, k_pos, k->n_tok)) return CPATTN_OK;
+    std::vector<BwdPair> pairs{BwdPair{q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv}};
+    return run_bwd(pairs, mask, scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int cpattn_ring_backward(int N, const cpattn_tensor* q_blocks, const cpattn_tensor* k_blocks,
+                                    const cpattn_tensor* v_blocks, const cpattn_posmap* pos, const cpattn_mask* mask,
+                                    float scale, const float* const* lse, const float* const* delta,
+                                    const cpattn_tensor* dout_blocks, float* const* dq, float* const* dk,
+                                    float* const* dv, void* stream) {
+    const char* who = "cpattn_ring_backward";
+    int rc;
+    if (N < 1 || N > 64) return fail(CPATTN_EINVAL, "%s: N = %d out of range [1, 64]", who, N);
+    if (!q_blocks || !k_blocks || !v_blocks || !pos || !lse || !delta || !dout_blocks || !dq || !dk || !dv)
+        return fail(CPATTN_EINVAL, "%s: NULL array argument", who);
+    if ((rc = check_scale(scale, who))) return rc;
+    for (int r = 0; r < N; ++r) {
+        if ((rc = check_qkv(&q_blocks[r], &k_blocks[r], &v_blocks[r], who))) return rc;
+        if ((rc = check_bwd_common(&q_blocks[r], &dout_blocks[r], mask, lse[r], delta[r], who))) return rc;
+        if (q_blocks[r].n_tok != k_blocks[r].n_tok)
+            return fail(CPATTN_EINVAL, "%s: rank %d holds %lld queries but %lld keys", who, r,
+                        (long long)q_blocks[r].n_tok, (long long)k_blocks[r].n_tok);
+        if (q_blocks[r].dtype != q_blocks[0].dtype || q_blocks[r].d != q_blocks[0].d ||
+            q_blocks[r].n_heads != q_blocks[0].n_heads || k_blocks[r].n_heads != k_blocks[0].n_heads)
+            return fail(CPATTN_EUNSUPPORTED, "%s: every block must share dtype, head dim and heads", who);
+        if ((rc = check_posmap(pos[r], k_blocks[r].n_tok, mask, who, "pos"))) return rc;
+        if (q_blocks[r].n_tok > 0 &&
+            ((rc = check_out(dq[r], lse[r], who)) || (rc = check_out(dk[r], delta[r], who)) ||
+             (rc = check_out(dv[r], delta[r], who))))
+            return rc;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // Round k: rank r's queries against the keys of rank (r - k) mod N.  Each
+    // round is a permutation of the blocks, so its pairs share neither a
+    // query block (dQ) nor a key block (dK, dV: the contributions that would
+    // travel back to the key's owner are added in place).
+    for (int k = 0; k < N; ++k) {
+        std::vector<BwdPair> pairs;
+        for (int r = 0; r < N; ++r) {
+            const int b = ((r - k) % N + N) % N;
+            if (!pair_nonempty(mask, pos[r], q_blocks[r].n_tok, pos[b], k_blocks[b].n_tok)) continue;
+            pairs.push_back(BwdPair{&q_blocks[r], &k_blocks[b], &v_blocks[b], &dout_blocks[r], pos[r], pos[b], lse[r],
+                                    delta[r], dq[r], dk[b], dv[b]});
+        }
+        if ((rc = run_bwd(pairs, mask, scale, st))) return rc;
+    }
+    return CPATTN_OK;
 }

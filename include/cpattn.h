@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 5
+#define CPATTN_VERSION_MINOR 6
 
 typedef enum {
     CPATTN_OK = 0,
@@ -224,6 +224,46 @@ int cpattn_ring_plan(int N, int C, const int64_t* n_tok, const cpattn_posmap* po
  * sizes or NULL pointers. */
 int cpattn_apply_sink(float* o, float* lse, const float* sink_logits, int64_t n_heads, int64_t n_rows,
                       int64_t d, void* stream);
+
+/* ---- backward ("Context Parallelism in ART", section 04) ----------------
+ * Gradients use the global softmax derivative: for a query with complete
+ * output o and log-sum-exp L (over ALL of its visible keys, i.e. the merged
+ * forward result) and output gradient g, D = dot(g, o) and for every visible
+ * key j of any stage: p_j = exp(s_j - L), dS_j = p_j (dot(g, v_j) - D),
+ * dV_j += p_j g, dQ += scale dS_j k_j, dK_j += scale dS_j q.  A stage needs
+ * only its own key block plus the query's L and D, and the stages'
+ * contributions add.  Sliding-window descriptors are EUNSUPPORTED here. */
+
+/* delta[h][i] = dot(dout[h][i][:], o[h][i][:]) for a complete output o
+ * (fp32 [H][n][d], contiguous) and output gradient dout (bf16 or fp32, same
+ * shape); delta: fp32 [H][n] device memory. */
+int cpattn_backward_delta(const float* o, const cpattn_tensor* dout, float* delta, void* stream);
+
+/* Gradient contributions of one (query block, key/value block) pair, ADDED to
+ * dq (fp32 [H][n_q][d]), dk and dv (fp32 [H_kv][n_k][d]); all contiguous
+ * device memory that the caller zero-fills before the first contribution.
+ * q, k, v, mask, positions and scale as in cpattn_partial; lse and delta:
+ * fp32 [H][n_q], the queries' complete LSE and D; dout: the output gradient
+ * of the queries (dtype, heads, tokens and d of q).  Grouped-query K/V are
+ * supported (every query head's contribution is added to its K/V head). */
+int cpattn_partial_backward(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                            const cpattn_mask* mask, cpattn_posmap q_pos, cpattn_posmap k_pos, float scale,
+                            const float* lse, const float* delta, const cpattn_tensor* dout,
+                            float* dq, float* dk, float* dv, void* stream);
+
+/* Backward of the ring emulated by cpattn_ring_emulate (all N ranks): in
+ * round k rank r's queries meet the keys of rank (r - k) mod N; rank r's dQ
+ * stays in dq[r], and the dK/dV contributions for rank b's keys, which a real
+ * ring returns to their owner, are added to dk[b], dv[b].  Each round is one
+ * dQ launch and one dK/dV launch (a round pairs every key block with one
+ * query block, so no two jobs of a launch write the same rows).  Host arrays
+ * of N entries: q_blocks, k_blocks, v_blocks, pos, lse, delta, dout_blocks,
+ * dq, dk, dv (device pointers, zero-filled by the caller). */
+int cpattn_ring_backward(int N, const cpattn_tensor* q_blocks, const cpattn_tensor* k_blocks,
+                         const cpattn_tensor* v_blocks, const cpattn_posmap* pos, const cpattn_mask* mask,
+                         float scale, const float* const* lse, const float* const* delta,
+                         const cpattn_tensor* dout_blocks, float* const* dq, float* const* dk, float* const* dv,
+                         void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* cpattn_last_error(void);

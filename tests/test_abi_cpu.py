@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_error_string(L):
     import context_blockwise_attention_amd as cp
-    assert cp.version() == (0, 5)
+    assert cp.version() == (0, 6)
     assert isinstance(L.cpattn_last_error(), bytes)
 
 

@@ -1,0 +1,169 @@
+"""Backward on the GPU (global softmax derivative, "Context Parallelism in
+ART", section 04) against the fp64 reference's backward, which is pinned by
+finite differences, the staged-sum invariant and the page's counterexample.
+
+The reference gradients use the reference's complete (O, L); the GPU uses the
+GPU forward's complete (O, L) and its own D = dot(dO, O).  Tolerances:
+fp32 inputs 1e-4 max-abs; bf16 inputs 1e-2 x the largest reference magnitude
+of each gradient (P and dS are rounded to bf16 for the MFMAs, a relative
+2^-9 per product term).
+
+* partial backward, causal and tree, fp32 and bf16, d 64 and 128, ragged
+  sizes and offsets, every element of dQ, dK, dV;
+* grouped-query K/V (8 query heads over 2);
+* ring backward of a packed tree (N = 4), every element;
+* the 64K tree ring at full size: the output gradient is nonzero on 256
+  sampled rows per head only, so dK and dV of every key come from those rows
+  (checked on every key) and dQ on those rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_blockwise_attention_amd as cpattn
+    cpattn.lib()
+    return cpattn
+
+
+def _check(name, got, ref, dtype):
+    got = got.double().cpu().numpy() if isinstance(got, torch.Tensor) else got
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    tol = 1e-4 if dtype == "f32" else 1e-2 * max(1.0, float(np.abs(ref).max()))
+    print("  %s: max|err| %.2e (tol %.1e, max|ref| %.2e)" % (name, err, tol, float(np.abs(ref).max())), flush=True)
+    assert err <= tol, name
+
+
+def _grad_out(seed, H, n, d, dtype):
+    g = torch.Generator().manual_seed(seed)
+    t = torch.randn((H, n, d), generator=g)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("maskname,nq,nk,qbase,kbase", [("causal", 300, 300, 0, 0), ("causal", 200, 333, 150, 100),
+                                                        ("tree", 300, 300, 0, 0)])
+def test_partial_backward(cp, dtype, d, maskname, nq, nk, qbase, kbase):
+    H = 2
+    q, _, _ = workloads.qkv(51, H, nq, d, dtype)
+    _, k, v = workloads.qkv(52, H, nk, d, dtype)
+    G = _grad_out(53, H, nq, d, dtype)
+    if maskname == "causal":
+        npos = max(qbase + nq, kbase + nk)
+        mask, omask = cp.Mask.causal(npos), oracle.Causal()
+    else:
+        seg, parent = workloads.tree_prompt_completions(100, (80, 70, 50))
+        mask, omask = cp.Mask.tree(seg, parent), oracle.Tree(seg, parent)
+    qpos, kpos = qbase + np.arange(nq), kbase + np.arange(nk)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    o, l = cp.partial(qd, kd, vd, mask, (qbase, 1), (kbase, 1))
+    delta = cp.backward_delta(o, gd)
+    dq, dk, dv = cp.partial_backward(qd, kd, vd, mask, l, delta, gd, (qbase, 1), (kbase, 1))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q, k, v, qpos, kpos, omask)
+    rq, rk, rv = oracle.attention_backward(q, k, v, qpos, kpos, O, L, G.double().numpy(), omask)
+    _check("dq", dq, rq, dtype)
+    _check("dk", dk, rk, dtype)
+    _check("dv", dv, rv, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_partial_backward_gqa(cp, dtype):
+    H, hkv, n, d = 8, 2, 260, 128
+    g = H // hkv
+    q, _, _ = workloads.qkv(54, H, n, d, dtype)
+    _, k, v = workloads.qkv(55, hkv, n, d, dtype)
+    G = _grad_out(56, H, n, d, dtype)
+    seg, parent = workloads.tree_prompt_completions(100, (60, 100))
+    mask, omask = cp.Mask.tree(seg, parent), oracle.Tree(seg, parent)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    o, l = cp.partial(qd, kd, vd, mask)
+    delta = cp.backward_delta(o, gd)
+    dq, dk, dv = cp.partial_backward(qd, kd, vd, mask, l, delta, gd)
+    torch.cuda.synchronize()
+    pos = np.arange(n)
+    kr, vr = k.repeat_interleave(g, 0), v.repeat_interleave(g, 0)
+    O, L = oracle.attention(q, kr, vr, pos, pos, omask)
+    rq, rk, rv = oracle.attention_backward(q, kr, vr, pos, pos, O, L, G.double().numpy(), omask)
+    _check("dq", dq, rq, dtype)
+    _check("dk", dk, rk.reshape(hkv, g, n, d).sum(1), dtype)
+    _check("dv", dv, rv.reshape(hkv, g, n, d).sum(1), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ring_backward_tree(cp, dtype):
+    N, H, d = 4, 2, 128
+    seg, parent = workloads.tree_prompt_completions(384, (128, 200, 96, 160))
+    n = len(seg) // N * N
+    seg = seg[:n]
+    c = n // N
+    q, k, v = workloads.qkv(57, H, n, d, dtype)
+    G = _grad_out(58, H, n, d, dtype)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    mask = cp.Mask.tree(seg, parent)
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    pos = [(r * c, 1) for r in range(N)]
+    out = cp.ring_emulate(blk(qd), blk(kd), blk(vd), pos, mask)
+    deltas = [cp.backward_delta(out[r][0], blk(gd)[r].contiguous()) for r in range(N)]
+    grads = cp.ring_backward(blk(qd), blk(kd), blk(vd), pos, mask, [out[r][1] for r in range(N)], deltas, blk(gd))
+    torch.cuda.synchronize()
+    allpos = np.arange(n)
+    omask = oracle.Tree(seg, parent)
+    O, L = oracle.attention(q, k, v, allpos, allpos, omask)
+    rq, rk, rv = oracle.attention_backward(q, k, v, allpos, allpos, O, L, G.double().numpy(), omask)
+    for name, i, ref in (("dq", 0, rq), ("dk", 1, rk), ("dv", 2, rv)):
+        got = torch.cat([grads[r][i] for r in range(N)], 1)
+        _check(name, got, ref, dtype)
+
+
+def test_tree64k_ring_backward_sampled(cp):
+    H, d, N = 32, 128, 4
+    seg, parent = workloads.tree_prompt_completions(24576, (8192,) * 5)
+    n = len(seg)
+    c = n // N
+    print("tree64k backward: generating inputs", flush=True)
+    q, k, v = workloads.qkv(0, H, n, d, "bf16")
+    rows = [workloads.sample_rows(0, h, n, forced=(0, n - 1, 24575, 24576, n - 8192)) for h in range(H)]
+    G = torch.zeros((H, n, d))
+    gen = torch.Generator().manual_seed(59)
+    for h in range(H):
+        G[h, torch.from_numpy(rows[h])] = torch.randn((len(rows[h]), d), generator=gen)
+    G = G.to(torch.bfloat16)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    mask = cp.Mask.tree(seg, parent)
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    pos = [(r * c, 1) for r in range(N)]
+    out = cp.ring_emulate(blk(qd), blk(kd), blk(vd), pos, mask)
+    deltas = [cp.backward_delta(out[r][0], blk(gd)[r].contiguous()) for r in range(N)]
+    grads = cp.ring_backward(blk(qd), blk(kd), blk(vd), pos, mask, [out[r][1] for r in range(N)], deltas, blk(gd))
+    dq = torch.cat([grads[r][0] for r in range(N)], 1)
+    dk = torch.cat([grads[r][1] for r in range(N)], 1)
+    dv = torch.cat([grads[r][2] for r in range(N)], 1)
+    torch.cuda.synchronize()
+    allpos = np.arange(n)
+    omask = oracle.Tree(seg, parent)
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    scale_ref = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for h in range(0, H, 8):   # 4 heads: the reference's dK/dV pass over all keys is the slow part
+        O, L = oracle.attention(q[h:h + 1], k[h:h + 1], v[h:h + 1], allpos, allpos, omask, rows=rows[h])
+        Gh = G[h:h + 1, torch.from_numpy(rows[h])].double().numpy()
+        rq, rk, rv = oracle.attention_backward(q[h:h + 1], k[h:h + 1], v[h:h + 1], allpos, allpos, O, L, Gh,
+                                               omask, rows=rows[h])
+        idx = torch.from_numpy(rows[h]).cuda()
+        for name, got, ref in (("dq", dq[h].index_select(0, idx), rq[0]), ("dk", dk[h], rk[0]), ("dv", dv[h], rv[0])):
+            worst[name] = max(worst[name], float(np.abs(got.double().cpu().numpy() - ref).max()))
+            scale_ref[name] = max(scale_ref[name], float(np.abs(ref).max()))
+    print("tree64k backward:", {k_: "%.2e / %.2e" % (worst[k_], scale_ref[k_]) for k_ in worst}, flush=True)
+    for name in worst:
+        assert worst[name] <= 1e-2 * max(1.0, scale_ref[name]), name
+    mask.free()
