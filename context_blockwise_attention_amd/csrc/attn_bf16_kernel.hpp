@@ -315,6 +315,16 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     };
     // softmax phase of one tile: mask (partial tiles), lazily raised max,
     // probabilities as the B operands of the next phase's PV MFMAs
+    // A masked score becomes -inf in the register that holds it: written as a
+    // tied asm operand, so that the masked and the unmasked paths leave the
+    // scores in the same registers (with a plain select the compiler gave the
+    // two paths different registers and copied all 32 scores on every full
+    // tile).  `keep` is the wave's lane mask of visible entries.
+    const float neg_inf = -INFINITY;
+    auto keep_if = [&](float x, uint64_t keep) {
+        asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(x) : "v"(neg_inf), "s"(keep));
+        return x;
+    };
     auto softmax_phase = [&](int tile, int full, const lds_byte* e_lds) {
         if (!full) {
             // key j (block index) is visible iff j <= jlim and, for trees,
@@ -340,9 +350,10 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                         }
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            bool vis = (jl0 + e <= lim) & (ypos < ends[e]);
-                            if (WIN) vis &= ly - lks[e] < args.mask.window;
-                            s[kb][hf * 8 + e] = vis ? s[kb][hf * 8 + e] : -INFINITY;
+                            uint64_t vis = __builtin_amdgcn_ballot_w64(jl0 + e <= lim) &
+                                           __builtin_amdgcn_ballot_w64(ypos < ends[e]);
+                            if (WIN) vis &= __builtin_amdgcn_ballot_w64(ly - lks[e] < args.mask.window);
+                            s[kb][hf * 8 + e] = keep_if(s[kb][hf * 8 + e], vis);
                         }
                     }
                 }
@@ -352,8 +363,9 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int jl = kb * 32 + (i >> 3) * 16 + (i & 7);
-                        const bool vis = WIN ? (jl <= lim) & (jl >= lo) : jl <= lim;
-                        s[kb][i] = vis ? s[kb][i] : -INFINITY;
+                        uint64_t vis = __builtin_amdgcn_ballot_w64(jl <= lim);
+                        if (WIN) vis &= __builtin_amdgcn_ballot_w64(jl >= lo);
+                        s[kb][i] = keep_if(s[kb][i], vis);
                     }
             }
         }
