@@ -17,6 +17,7 @@
 
 #include "../../include/cpattn.h"
 #include "attn_bf16_kernel.hpp"
+#include "attn_bwd_bf16_kernel.hpp"
 #include "attn_bwd_kernel.hpp"
 #include "attn_kernel.hpp"
 #include "merge_kernel.hpp"
@@ -762,10 +763,13 @@ extern "C" int cpattn_apply_sink(float* o, float* lse, const float* sink_logits,
 template <typename T, int D>
 static int launch_bwd_t(BwdArgs& a, bool dkv, hipStream_t st) {
     using S = BwdStage<T, D>;
-    const int smem_dq = (2 * S::ROW_ELEMS + S::T_ELEMS) * (int)sizeof(T) + kBwdTile * 4;
-    const int smem_dkv = (2 * S::ROW_ELEMS + 2 * S::T_ELEMS) * (int)sizeof(T) + 2 * kBwdTile * 4;
-    const auto kq = attn_bwd_dq_kernel<T, D>;
-    const auto kkv = attn_bwd_dkv_kernel<T, D>;
+    constexpr bool bf16 = sizeof(T) == 2;
+    const int smem_dq = bf16 ? BwdDqBf16Smem<D>::BYTES : (2 * S::ROW_ELEMS + S::T_ELEMS) * (int)sizeof(T) + kBwdTile * 4;
+    const int smem_dkv =
+        bf16 ? BwdDkvBf16Smem<D>::BYTES : (2 * S::ROW_ELEMS + 2 * S::T_ELEMS) * (int)sizeof(T) + 2 * kBwdTile * 4;
+    // bf16: tiles loaded straight into LDS, transposed operands read with ds_read_b64_tr_b16
+    const auto kq = bf16 ? attn_bwd_dq_bf16_kernel<D> : attn_bwd_dq_kernel<T, D>;
+    const auto kkv = bf16 ? attn_bwd_dkv_bf16_kernel<D> : attn_bwd_dkv_kernel<T, D>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kq),

@@ -1,0 +1,506 @@
+// attn_bwd_bf16_kernel.hpp -- backward of partial attention for bf16 inputs
+// on gfx950, built on the same CDNA4 features as the bf16 forward kernel.
+//
+// Arithmetic and work split as in attn_bwd_kernel.hpp ("Context Parallelism
+// in ART", section 04: p = exp(s - L) with the complete L, dS = p (dP - D)).
+// What differs is how a tile reaches the matrix cores:
+//
+//  * Tiles of 32 rows go from HBM straight into LDS with buffer_load ... lds,
+//    double buffered: the loads of tile t+1 are issued right after the one
+//    workgroup barrier of iteration t and land while tile t is computed.
+//  * A tile is stored once, row-major.  Operands that need rows (K and V rows
+//    for S^T = K Q^T and dP^T = V dO^T) are 16-byte row reads; operands that
+//    need columns (K^T for dQ^T += K^T dS^T) are read from the same rows with
+//    ds_read_b64_tr_b16.  The 16-byte chunks of a row are XOR-swizzled by
+//    bwd_swizzle so that both access patterns spread over all LDS banks.
+#pragma once
+
+#include "attn_bf16_kernel.hpp"
+#include "attn_bwd_kernel.hpp"
+
+namespace cpattn {
+
+// 32-row bf16 tile of D columns in LDS (row-major, swizzled 16-byte chunks)
+template <int D>
+struct BwdTileBf16 {
+    static constexpr int ROWS = kBwdTile;
+    static constexpr int ROWB = D * 2;                  // bytes per row
+    static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+    static constexpr int BYTES = ROWS * ROWB;
+    static constexpr int RPB = 1024 / ROWB;             // rows per 1 KB direct load (64 lanes x 16 B)
+    static constexpr int LOADS = BYTES / 1024;          // direct loads per tile
+    static constexpr int LOADS_PER_WAVE = LOADS / 4;    // four waves share a tile
+    static constexpr int DSTEPS = D / 16;
+    static constexpr int DBLK = D / 32;
+    static_assert(LOADS % 4 == 0, "tile shape");
+};
+
+// Physical chunk of logical chunk c in row r (row within a tile) is
+// c ^ bwd_swizzle(r).  Row reads: the 8 rows that 8 consecutive lanes read
+// (r32 0-7 -> rows 0-3, 8-11 in the permuted order; likewise per 16 lanes)
+// get distinct swizzles.  Transposed reads: a 16-lane group reads rows
+// 8g + kq (kq 0-3) at chunks base ^ t (t 0-1), and swizzle >> 1 differs
+// between those rows, so the 8 (row, t) chunks are distinct.  For 64-column
+// rows two rows share one 256-byte bank window, so the swizzle is spread over
+// row pairs instead.
+template <int D>
+__device__ __forceinline__ int bwd_swizzle(int r) {
+    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
+// Per-lane offsets of one wave's share of a tile's direct loads: load i of
+// wave w fills 1 KB block b = 4 i + w, lane L goes to row b RPB + L / CPR,
+// physical chunk L % CPR, so it fetches logical chunk (L % CPR) ^ swizzle.
+template <int D>
+struct BwdDma {
+    using TT = BwdTileBf16<D>;
+    int voff[TT::LOADS_PER_WAVE];
+    __device__ __forceinline__ void init(int wave, int lane, int st) {
+#pragma unroll
+        for (int i = 0; i < TT::LOADS_PER_WAVE; ++i) {
+            const int row = (4 * i + wave) * TT::RPB + lane / TT::CPR;
+            voff[i] = row * st * 2 + (((lane % TT::CPR) ^ bwd_swizzle<D>(row)) * 16);
+        }
+    }
+    // rows row0 .. row0 + 31 of the buffer into the tile at `dst`
+    __device__ __forceinline__ void issue(const i32x4& rsrc, int row0, int st, int wave, lds_byte* dst) const {
+        const int base = row0 * st * 2;
+#pragma unroll
+        for (int i = 0; i < TT::LOADS_PER_WAVE; ++i)
+            dma_b128(rsrc, voff[i] + base, lds_addr(dst + (4 * i + wave) * 1024));
+    }
+};
+
+// 16-byte read of logical chunk 2 ds + g of a row: the row's byte offset plus
+// the physical chunk, (2 ds + g) ^ swizzle = 2 ds ^ (g ^ swizzle)
+struct BwdRowRead {
+    int base;   // row * bytes per row
+    int x;      // g ^ swizzle(row)
+    __device__ __forceinline__ int off(int ds) const { return base + (((2 * ds) ^ x) << 4); }
+};
+
+// LDS offsets of the two operand reads a lane makes from a tile:
+//  row: 16-byte reads of row `perm` (the MFMA row order), chunk 2 ds + g
+//  tr_lo[b], tr_hi[b]: the ds_read_b64_tr_b16 pair that builds the A operand
+//  (column block b of the tile's transpose, rows 0-15 of the k-step), as in
+//  the forward's V^T reads
+template <int D>
+struct BwdReadOffsets {
+    using TT = BwdTileBf16<D>;
+    BwdRowRead row;
+    int tr_lo[TT::DBLK], tr_hi[TT::DBLK];
+    __device__ __forceinline__ void init(int lane, int perm) {
+        const int g = lane >> 5;
+        row = BwdRowRead{perm * TT::ROWB, g ^ bwd_swizzle<D>(perm)};
+        const int G2 = (lane >> 4) & 1;
+        const int kq = (lane & 15) >> 2;
+        const int qq = lane & 3;
+        const int rlo = 8 * g + kq, rhi = rlo + 4;
+#pragma unroll
+        for (int b = 0; b < TT::DBLK; ++b) {
+            const int c = 4 * b + 2 * G2 + (qq >> 1);
+            tr_lo[b] = rlo * TT::ROWB + ((c ^ bwd_swizzle<D>(rlo)) * 16) + (qq & 1) * 8;
+            tr_hi[b] = rhi * TT::ROWB + ((c ^ bwd_swizzle<D>(rhi)) * 16) + (qq & 1) * 8;
+        }
+    }
+};
+
+// A operand of a transposed product: column block b, k-step ks of the tile
+template <int D>
+__device__ __forceinline__ bf16x8 bwd_tr_operand(const lds_byte* tile, const BwdReadOffsets<D>& o, int ks, int b) {
+    const lds_byte* p = tile + ks * 16 * BwdTileBf16<D>::ROWB;
+    const u32x2 lo = lds_tr4(p + o.tr_lo[b]);
+    const u32x2 hi = lds_tr4(p + o.tr_hi[b]);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+__device__ __forceinline__ void bwd_tile_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
+// dQ (bf16): 128 query rows per workgroup, 32-key tiles
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdDqBf16Smem {
+    using TT = BwdTileBf16<D>;
+    static constexpr int K_OFF = 0;
+    static constexpr int V_OFF = 2 * TT::BYTES;
+    static constexpr int E_OFF = 4 * TT::BYTES;   // two 256-byte horizon slots (64-lane loads)
+    static constexpr int BYTES = E_OFF + 2 * 256;
+};
+
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_bf16_kernel(const BwdArgs args) {
+    using TT = BwdTileBf16<D>;
+    using SM = BwdDqBf16Smem<D>;
+    constexpr int BN = kBwdTile;
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+    int ji, head, qtile;
+    if (!bwd_item(args, blockIdx.x, &ji, &head, &qtile)) return;
+    ji = wave_uniform(ji);
+    head = wave_uniform(head);
+    qtile = wave_uniform(qtile);
+    const BwdJob& J = args.jobs[ji];
+    const KeyBlock kblk{J.kbase, J.kstride, J.n_k};
+    const int k_st = J.k_st, v_st = J.v_st;
+    const int kvh = head / J.kv_group;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = wave_uniform(tid >> 6);
+    const int r32 = lane & 31;
+    const int g = lane >> 5;
+    const int q_first = qtile * kBwdRows;
+    const int q_last = min(q_first + kBwdRows, J.n_q) - 1;
+    const int y0 = J.qbase + J.qstride * q_first;
+    const int y1 = J.qbase + J.qstride * q_last;
+    const int qi = q_first + wave * 32 + r32;
+    const int ypos = J.qbase + J.qstride * qi;
+    const bool tree = args.mask.kind == kTree;
+
+    const __bf16* qh = reinterpret_cast<const __bf16*>(J.q) + head * J.q_sh;
+    const __bf16* doh = reinterpret_cast<const __bf16*>(J.dout) + head * J.do_sh;
+    const __bf16* kh = reinterpret_cast<const __bf16*>(J.k) + kvh * J.k_sh;
+    const __bf16* vh = reinterpret_cast<const __bf16*>(J.v) + kvh * J.v_sh;
+
+    bf16x8 qreg[TT::DSTEPS], doreg[TT::DSTEPS];
+    {
+        const auto qr = make_rsrc(qh, ((J.n_q - 1) * J.q_st + D) * 2);
+        const auto dor = make_rsrc(doh, ((J.n_q - 1) * J.do_st + D) * 2);
+#pragma unroll
+        for (int s = 0; s < TT::DSTEPS; ++s) {
+            qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(qr, (qi * J.q_st + s * 16 + 8 * g) * 2));
+            doreg[s] = __builtin_bit_cast(bf16x8, buf_load16(dor, (qi * J.do_st + s * 16 + 8 * g) * 2));
+        }
+    }
+    const bool valid_q = qi < J.n_q;
+    const float lse = valid_q ? J.lse[(int64_t)head * J.n_q + qi] : -INFINITY;
+    // exp2(s c2 - lse2) is 0 for a row without gradient (no visible key, or past the block)
+    const float lse2 = lse > -INFINITY ? lse * 1.4426950408889634f : INFINITY;
+    const float dlt = valid_q ? J.delta[(int64_t)head * J.n_q + qi] : 0.f;
+    const float c2 = args.scale_log2;
+    const int jlim = min(J.n_k - 1, ypos < J.kbase ? -1 : (ypos - J.kbase) / J.kstride);
+
+    lds_byte* const lds = to_lds(smem);
+    const i32x4 k_rsrc = sgpr_rsrc(kh, (J.n_k - 1) * k_st * 2 + D * 2);
+    const i32x4 v_rsrc = sgpr_rsrc(vh, (J.n_k - 1) * v_st * 2 + D * 2);
+    const i32x4 e_rsrc = sgpr_rsrc(args.mask.end, args.mask.n_pos * 4);
+    BwdDma<D> dk, dv;
+    dk.init(wave, lane, k_st);
+    dv.init(wave, lane, v_st);
+    BwdReadOffsets<D> ro;
+    ro.init(lane, mfma_row_perm(r32));
+    auto issue = [&](int tile, int slot) {
+        dk.issue(k_rsrc, tile * BN, k_st, wave, lds + SM::K_OFF + slot * TT::BYTES);
+        dv.issue(v_rsrc, tile * BN, v_st, wave, lds + SM::V_OFF + slot * TT::BYTES);
+        if (tree && wave == 0)
+            dma_b32(e_rsrc, (kblk.kbase + kblk.kstride * (tile * BN + lane)) * 4, lds_addr(lds + SM::E_OFF + slot * 256));
+    };
+
+    f32x16 acc[TT::DBLK];
+#pragma unroll
+    for (int b = 0; b < TT::DBLK; ++b) acc[b] = f32x16{};
+
+    TileCursor<BN> cur;
+    cur.init(kblk, args.mask, y0, y1);
+    int t_cur, f_cur, t_nxt = 0, f_nxt = 0;
+    if (cur.next(kblk, args.mask, y1, &t_cur, &f_cur)) {
+        issue(t_cur, 0);
+        bool h_nxt = cur.next(kblk, args.mask, y1, &t_nxt, &f_nxt);
+        for (int it = 0;; ++it) {
+            const int slot = it & 1;
+            // this wave's loads of the current tile have landed; after the
+            // barrier every wave's have, and every wave is done with the
+            // other slot (read in the previous iteration)
+            __builtin_amdgcn_s_waitcnt(0xF70);
+            bwd_tile_barrier();
+            if (h_nxt) issue(t_nxt, slot ^ 1);
+            const lds_byte* kt = lds + SM::K_OFF + slot * TT::BYTES;
+            const lds_byte* vt = lds + SM::V_OFF + slot * TT::BYTES;
+
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int ds = 0; ds < TT::DSTEPS; ++ds) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kt + ro.row.off(ds)), qreg[ds], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(vt + ro.row.off(ds)), doreg[ds], dp, 0, 0, 0);
+            }
+            // lane value i is key 16 (i / 8) + 8 g + i % 8 of the tile
+            bf16x8 dsb[2];
+            if (f_cur) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2));
+                    dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dlt));
+                }
+            } else {
+                const int lim = jlim - t_cur * BN - 8 * g;
+                const auto* ep = reinterpret_cast<const __attribute__((address_space(3))) int*>(lds + SM::E_OFF + slot * 256) + 8 * g;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int jl = (i >> 3) * 16 + (i & 7);   // + 8 g, folded into lim and ep
+                    bool vis = jl <= lim;
+                    if (tree) vis = vis && ypos < ep[jl];
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2)) : 0.f;
+                    dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dlt));
+                }
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int b = 0; b < TT::DBLK; ++b)
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_operand<D>(kt, ro, ks, b), dsb[ks], acc[b],
+                                                                     0, 0, 0);
+            if (!h_nxt) break;
+            t_cur = t_nxt;
+            f_cur = f_nxt;
+            h_nxt = cur.next(kblk, args.mask, y1, &t_nxt, &f_nxt);
+        }
+    }
+
+    if (!valid_q) return;
+    // lane (query qi, half g) holds dQ^T[d][qi] for d = 32 b + 8 (i / 4) + 4 g + i % 4
+    float* row = J.dq + ((int64_t)head * J.n_q + qi) * D;
+    const float sc = args.scale;
+#pragma unroll
+    for (int b = 0; b < TT::DBLK; ++b)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4* dst = reinterpret_cast<f32x4*>(row + b * 32 + q4 * 8 + g * 4);
+            f32x4 v = *dst;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += sc * acc[b][q4 * 4 + e];
+            *dst = v;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV (bf16): 128 keys per workgroup (32 per wave), 32-query tiles
+//
+// A wave keeps its keys' K rows in registers (the B operand of S = Q K^T) and
+// the workgroup's V rows in LDS (B operand of dP = dO V^T, read per tile), so
+// that K, the dK/dV accumulators and one tile's S and dP fit the 256
+// registers of two waves per SIMD.  Query tiles (Q, dO and the rows' LSE and
+// D) stream through two LDS slots.  For a tree stored in depth-first preorder
+// key x is visible exactly to the query positions [x, end[x]): the tiles are
+// those from the first key's position to the largest horizon, and a tile is
+// full when its first query lies at or after the last key and its last query
+// before the smallest horizon.
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdDkvBf16Smem {
+    using TT = BwdTileBf16<D>;
+    static constexpr int V_OFF = 0;                       // 128 V rows, 4 tiles of 32
+    static constexpr int Q_OFF = 4 * TT::BYTES;           // two slots
+    static constexpr int DO_OFF = Q_OFF + 2 * TT::BYTES;  // two slots
+    static constexpr int L_OFF = DO_OFF + 2 * TT::BYTES;  // LSE, two 256-byte slots (64-lane loads)
+    static constexpr int DL_OFF = L_OFF + 2 * 256;        // D, two slots
+    static constexpr int R_OFF = DL_OFF + 2 * 256;        // per-wave reductions
+    static constexpr int BYTES = R_OFF + 64;
+};
+
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
+    using TT = BwdTileBf16<D>;
+    using SM = BwdDkvBf16Smem<D>;
+    constexpr int BM = kBwdTile;
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+    int ji, kvh, ktile;
+    if (!bwd_item(args, blockIdx.x, &ji, &kvh, &ktile)) return;
+    ji = wave_uniform(ji);
+    kvh = wave_uniform(kvh);
+    ktile = wave_uniform(ktile);
+    const BwdJob& J = args.jobs[ji];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = wave_uniform(tid >> 6);
+    const int r32 = lane & 31;
+    const int g = lane >> 5;
+    const bool tree = args.mask.kind == kTree;
+    const int j0 = ktile * kBwdRows;
+    const int jk = j0 + wave * 32 + r32;          // this lane's key
+    const bool valid_k = jk < J.n_k;
+    const int kpos = J.kbase + J.kstride * jk;
+    // key jk is visible to the query positions [kpos, horizon)
+    const int horizon = !valid_k ? (int)0x80000000 : tree ? args.mask.end[kpos] : 0x7fffffff;
+
+    const __bf16* kh = reinterpret_cast<const __bf16*>(J.k) + kvh * J.k_sh;
+    const __bf16* vh = reinterpret_cast<const __bf16*>(J.v) + kvh * J.v_sh;
+    bf16x8 kreg[TT::DSTEPS];
+    {
+        const auto kr = make_rsrc(kh, ((J.n_k - 1) * J.k_st + D) * 2);
+#pragma unroll
+        for (int s = 0; s < TT::DSTEPS; ++s)
+            kreg[s] = __builtin_bit_cast(bf16x8, buf_load16(kr, (jk * J.k_st + s * 16 + 8 * g) * 2));
+    }
+    lds_byte* const lds = to_lds(smem);
+    const int q_st = J.q_st, do_st = J.do_st;
+    BwdDma<D> dma_q, dma_do;
+    dma_q.init(wave, lane, q_st);
+    dma_do.init(wave, lane, do_st);
+    {
+        // the workgroup's 128 V rows, as four 32-row tiles
+        BwdDma<D> dma_v;
+        dma_v.init(wave, lane, J.v_st);
+        const i32x4 v_rsrc = sgpr_rsrc(vh, (J.n_k - 1) * J.v_st * 2 + D * 2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dma_v.issue(v_rsrc, j0 + t * 32, J.v_st, wave, lds + SM::V_OFF + t * TT::BYTES);
+    }
+
+    // query rows that can see a key of the workgroup: positions from the first
+    // key's to the largest horizon; the full-tile bounds: last key position and
+    // smallest horizon over the valid keys
+    int hmax = horizon, hmin = valid_k ? horizon : 0x7fffffff, kmax = valid_k ? kpos : (int)0x80000000;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        hmax = max(hmax, __shfl_xor(hmax, off));
+        hmin = min(hmin, __shfl_xor(hmin, off));
+        kmax = max(kmax, __shfl_xor(kmax, off));
+    }
+    int* red = reinterpret_cast<int*>(smem + SM::R_OFF);
+    if (lane == 0) {
+        red[wave] = hmax;
+        red[4 + wave] = hmin;
+        red[8 + wave] = kmax;
+    }
+    __syncthreads();
+    hmax = wave_uniform(max(max(red[0], red[1]), max(red[2], red[3])));
+    hmin = wave_uniform(min(min(red[4], red[5]), min(red[6], red[7])));
+    kmax = wave_uniform(max(max(red[8], red[9]), max(red[10], red[11])));
+    const int pos_lo = J.kbase + J.kstride * j0;
+    auto first_query_at_or_after = [&](int64_t x) -> int {
+        if (x <= J.qbase) return 0;
+        const int64_t i = (x - J.qbase + J.qstride - 1) / J.qstride;
+        return (int)min<int64_t>(i, J.n_q);
+    };
+    const int i_begin = first_query_at_or_after(pos_lo) / BM * BM;
+    const int i_end = hmax == (int)0x80000000 ? 0 : first_query_at_or_after((int64_t)hmax);   // exclusive
+    const int n_tiles = i_end > i_begin ? (i_end - i_begin + BM - 1) / BM : 0;
+    const int steps = n_tiles * J.kv_group;   // (query head, tile) pairs, head-major
+
+    f32x16 acck[TT::DBLK], accv[TT::DBLK];
+#pragma unroll
+    for (int b = 0; b < TT::DBLK; ++b) {
+        acck[b] = f32x16{};
+        accv[b] = f32x16{};
+    }
+    BwdReadOffsets<D> ro;
+    ro.init(lane, mfma_row_perm(r32));
+    // B operand rows of dP: this wave's 32 V rows (tile `wave` of the V block) in natural order
+    const BwdRowRead vread{SM::V_OFF + wave * TT::BYTES + r32 * TT::ROWB, g ^ bwd_swizzle<D>(r32)};
+
+    auto issue = [&](int step, int slot) {
+        const int hq = step / n_tiles;
+        const int q0 = i_begin + (step - hq * n_tiles) * BM;
+        const int head = kvh * J.kv_group + hq;
+        const __bf16* qh = reinterpret_cast<const __bf16*>(J.q) + head * J.q_sh;
+        const __bf16* doh = reinterpret_cast<const __bf16*>(J.dout) + head * J.do_sh;
+        dma_q.issue(sgpr_rsrc(qh, (J.n_q - 1) * q_st * 2 + D * 2), q0, q_st, wave, lds + SM::Q_OFF + slot * TT::BYTES);
+        dma_do.issue(sgpr_rsrc(doh, (J.n_q - 1) * do_st * 2 + D * 2), q0, do_st, wave,
+                     lds + SM::DO_OFF + slot * TT::BYTES);
+        if (wave == 0)
+            dma_b32(sgpr_rsrc(J.lse + (int64_t)head * J.n_q, J.n_q * 4), (q0 + lane) * 4,
+                    lds_addr(lds + SM::L_OFF + slot * 256));
+        else if (wave == 1)
+            dma_b32(sgpr_rsrc(J.delta + (int64_t)head * J.n_q, J.n_q * 4), (q0 + lane) * 4,
+                    lds_addr(lds + SM::DL_OFF + slot * 256));
+    };
+
+    const float c2 = args.scale_log2;
+    if (steps > 0) issue(0, 0);
+    for (int step = 0; step < steps; ++step) {
+        const int slot = step & 1;
+        // this wave's loads of the current tile (and, first, the V block)
+        // have landed; after the barrier every wave's have, and the other slot
+        // is free
+        __builtin_amdgcn_s_waitcnt(0xF70);
+        bwd_tile_barrier();
+        if (step + 1 < steps) issue(step + 1, slot ^ 1);
+        const int q0 = i_begin + (step % n_tiles) * BM;
+        const lds_byte* qt = lds + SM::Q_OFF + slot * TT::BYTES;
+        const lds_byte* dt = lds + SM::DO_OFF + slot * TT::BYTES;
+
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ds = 0; ds < TT::DSTEPS; ++ds) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(qt + ro.row.off(ds)), kreg[ds], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(dt + ro.row.off(ds)), lds_op(lds + vread.off(ds)), dp, 0, 0,
+                                                         0);
+        }
+        // lane (key jk, half g), value i: query row q0 + il, il = 16 (i / 8) + 8 g + i % 8
+        const auto* lp = reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + SM::L_OFF + slot * 256) + 8 * g;
+        const auto* dlp = reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + SM::DL_OFF + slot * 256) + 8 * g;
+        const int yq0 = J.qbase + J.qstride * q0;
+        const int yq1 = J.qbase + J.qstride * min(q0 + BM - 1, J.n_q - 1);
+        const bool full = yq0 >= kmax && (!tree || yq1 < hmin);
+        bf16x8 pb[2], dsb[2];
+        // a row without gradient (LSE = -inf) gets p = 0
+        auto prob = [&](int i, int il) {
+            const float lse = lp[il];
+            const float l2 = lse > -INFINITY ? lse * 1.4426950408889634f : INFINITY;
+            return __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
+        };
+        if (full) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int il = (i >> 3) * 16 + (i & 7);   // + 8 g, folded into lp, dlp
+                const float p = prob(i, il);
+                pb[i >> 3][i & 7] = (__bf16)p;
+                dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dlp[il]));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int il = (i >> 3) * 16 + (i & 7);
+                const int qrow = q0 + il + 8 * g;
+                const int y = J.qbase + J.qstride * qrow;
+                const bool vis = qrow < J.n_q && kpos <= y && y < horizon;
+                const float p = vis ? prob(i, il) : 0.f;
+                pb[i >> 3][i & 7] = (__bf16)p;
+                dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dlp[il]));
+            }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int b = 0; b < TT::DBLK; ++b) {
+                accv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_operand<D>(dt, ro, st, b), pb[st], accv[b], 0,
+                                                                  0, 0);
+                acck[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_operand<D>(qt, ro, st, b), dsb[st], acck[b],
+                                                                  0, 0, 0);
+            }
+    }
+
+    if (!valid_k) return;
+    // lane (key jk, half g) holds dK^T / dV^T [d][jk] for d = 32 b + 8 (i / 4) + 4 g + i % 4
+    float* krow = J.dk + ((int64_t)kvh * J.n_k + jk) * D;
+    float* vrow = J.dv + ((int64_t)kvh * J.n_k + jk) * D;
+    const float sc = args.scale;
+#pragma unroll
+    for (int b = 0; b < TT::DBLK; ++b)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int c = b * 32 + q4 * 8 + g * 4;
+            f32x4 kv = *reinterpret_cast<f32x4*>(krow + c);
+            f32x4 vv = *reinterpret_cast<f32x4*>(vrow + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kv[e] += sc * acck[b][q4 * 4 + e];
+                vv[e] += accv[b][q4 * 4 + e];
+            }
+            *reinterpret_cast<f32x4*>(krow + c) = kv;
+            *reinterpret_cast<f32x4*>(vrow + c) = vv;
+        }
+}
+
+}  // namespace cpattn
