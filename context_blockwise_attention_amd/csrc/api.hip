@@ -810,7 +810,7 @@ static int run_bwd(const std::vector<BwdPair>& pairs, const cpattn_mask* m, floa
             a.scale = scale;
             a.scale_log2 = scale * 1.4426950408889634f;
             a.n_jobs = (int32_t)n;
-            int64_t wg = 0;
+            int64_t sum_tiles = 0;
             int dtype = 0, d = 0;
             for (size_t i = 0; i < n; ++i) {
                 const BwdPair& P = pairs[first + i];
@@ -842,10 +842,14 @@ static int run_bwd(const std::vector<BwdPair>& pairs, const cpattn_mask* m, floa
                 const int64_t rows = dkv ? P.k->n_tok : P.q->n_tok;
                 j.tiles = (int32_t)((rows + kBwdRows - 1) / kBwdRows);
                 a.heads = (int32_t)(dkv ? P.k->n_heads : P.q->n_heads);
-                wg += (int64_t)a.heads * j.tiles;
+                sum_tiles += j.tiles;
                 dtype = P.q->dtype;
                 d = (int)P.q->d;
             }
+            // (all pairs of a call have the same head counts: checked by the callers)
+            a.heads_per_xcd = a.heads >= 8 ? (a.heads + 7) / 8 : 0;
+            a.last_first = dkv ? 0 : 1;
+            const int64_t wg = sum_tiles * (a.heads_per_xcd > 0 ? 8 * (int64_t)a.heads_per_xcd : (int64_t)a.heads);
             if (wg > INT32_MAX / 2) return fail(CPATTN_EUNSUPPORTED, "too many workgroups in one launch");
             a.total_wg = (int32_t)wg;
             int rc = launch_bwd(a, dkv == 1, dtype, d, st);

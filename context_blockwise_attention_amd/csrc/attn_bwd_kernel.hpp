@@ -61,19 +61,34 @@ struct BwdArgs {
     MaskArgs mask;
     int32_t n_jobs;
     int32_t heads;        // heads the kernel iterates over (query heads for dQ, K/V heads for dK/dV)
+    int32_t heads_per_xcd;   // ceil(heads / 8) with at least 8 heads, else 0
+    int32_t last_first;   // 1: a head's tiles from the last (dQ: later queries see more keys), 0: from the first (dK/dV)
     int32_t total_wg;
     float scale;
     float scale_log2;     // scale * log2(e)
 };
 
+// Workgroup -> (job, head, tile), mapped like the forward's work_item: with at
+// least 8 heads, XCD x (= bid mod 8) runs its own heads one after another, so
+// the workgroups in flight on an XCD stream the same head's tiles through its
+// L2; a head's heaviest tiles go first.
 __device__ __forceinline__ bool bwd_item(const BwdArgs& a, int bid, int* job, int* head, int* tile) {
-    int p = bid;
+    const bool by_xcd = a.heads_per_xcd > 0;
+    const int x = bid & 7;
+    int p = by_xcd ? (bid >> 3) : bid;
+    const int hg = by_xcd ? a.heads_per_xcd : a.heads;
+    const bool ranges = by_xcd && (a.heads & 7) == 0;
     for (int j = 0; j < a.n_jobs; ++j) {
-        const int n = a.heads * a.jobs[j].tiles;
+        const int nt = a.jobs[j].tiles;
+        const int n = hg * nt;
         if (p < n) {
+            const int hi = p / nt;
+            const int r = p - hi * nt;
+            const int h = !by_xcd ? hi : ranges ? x * hg + hi : x + 8 * hi;
+            if (h >= a.heads) return false;
             *job = j;
-            *head = p / a.jobs[j].tiles;
-            *tile = a.jobs[j].tiles - 1 - (p % a.jobs[j].tiles);   // later (heavier for causal dQ) tiles first
+            *head = h;
+            *tile = a.last_first ? nt - 1 - r : r;
             return true;
         }
         p -= n;
