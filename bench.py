@@ -489,8 +489,41 @@ def main():
     result["sink"] = {"kernel": "sink_kernel", "rows": H * n, "d": d, "ms": round(sink_ms, 4), "bytes": sink_bytes,
                       "GB/s": round(sink_bytes / (sink_ms * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round(sink_bytes / (sink_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    # adjoints of the sink and of a 4-part merge on the same rows (HBM-bound)
+    g_y = torch.randn(so.shape, generator=torch.Generator(device="cpu").manual_seed(3)).to(dev)
+    sb_ms = _time_reps(torch, stream, reps, lambda: cp.sink_backward(so, sl, sink, g_y))
+    sb_bytes = H * n * (3 * d + 2) * 4 + H * 4
+    result["sink_backward"] = {"kernel": "sink_backward_kernel + sink_grad_kernel", "rows": H * n, "d": d,
+                               "ms": round(sb_ms, 4), "bytes": sb_bytes,
+                               "GB/s": round(sb_bytes / (sb_ms * 1e-3) / 1e9, 1),
+                               "frac_of_hbm_peak": round(sb_bytes / (sb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    mb_rows = H * c
+    mparts = [(outs[r][0], outs[r][1]) for r in range(N)]   # N partials of one rank's size
+    mo, ml = cp.merge(mparts)
+    mb_outs = [(torch.empty_like(mo), torch.empty_like(ml)) for _ in range(N)]
+    g_m = so[:, :c].contiguous()
+    mb_ms = _time_reps(torch, stream, reps, lambda: cp.merge_backward(mparts, (mo, ml), g_m, outs=mb_outs))
+    # per row: reads N (d + 1) + 2 d + 1 floats, writes N (d + 1)
+    mb_bytes = mb_rows * (N * (d + 1) + 2 * d + 1 + N * (d + 1)) * 4
+    result["merge_backward"] = {"kernel": "merge_backward_kernel", "parts": N, "rows": mb_rows, "d": d,
+                                "ms": round(mb_ms, 4), "bytes": mb_bytes,
+                                "GB/s": round(mb_bytes / (mb_ms * 1e-3) / 1e9, 1),
+                                "frac_of_hbm_peak": round(mb_bytes / (mb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     mask.free()
     print(json.dumps(result), flush=True)
+
+
+def _time_reps(torch, stream, reps, fn):
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 if __name__ == "__main__":

@@ -88,10 +88,13 @@ def lib():
                                                                                P, P, ctypes.POINTER(_Tensor), P, P, P,
                                                                                P]
         L.cpattn_ring_backward.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P]
+        L.cpattn_merge_backward.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int64, P, P, P, P, P, P, P]
+        L.cpattn_sink_backward.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P, P, P]
         for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
                   "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan",
                   "cpattn_apply_sink", "cpattn_mask_with_window", "cpattn_backward_delta",
-                  "cpattn_partial_backward", "cpattn_ring_backward"):
+                  "cpattn_partial_backward", "cpattn_ring_backward", "cpattn_merge_backward",
+                  "cpattn_sink_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -363,6 +366,55 @@ def apply_sink(o: torch.Tensor, lse: torch.Tensor, sink_logits: torch.Tensor, st
     _check(lib().cpattn_apply_sink(o.data_ptr(), lse.data_ptr(), sink_logits.data_ptr(), H, n, d,
                                    _stream(stream)))
     return o, lse
+
+
+def merge_backward(parts, merged, g_o, g_lse=None, outs=None, stream=None):
+    """Adjoints of :func:`merge`: for parts ``[(O_p, LSE_p)]`` merged into
+    ``merged = (O, LSE)``, output gradient ``g_o`` and optional LSE gradient
+    ``g_lse``, returns ``[(dO_p, dLSE_p)]`` (fp32, shapes of the parts)."""
+    parts = list(parts)
+    if not parts:
+        raise ValueError("no parts")
+    o, lse = merged
+    d = o.shape[-1]
+    rows = lse.numel()
+    for t, name in [(o, "o"), (lse, "lse"), (g_o, "g_o")] + [(g_lse, "g_lse")] * (g_lse is not None):
+        _f32_dev(t, name)
+    if g_o.shape != o.shape or (g_lse is not None and g_lse.shape != lse.shape):
+        raise ValueError("gradient shapes differ from the merged result")
+    for po, pl in parts:
+        if po.shape != o.shape or pl.shape != lse.shape:
+            raise ValueError("parts must have the merged result's shapes")
+        _f32_dev(po, "o_p")
+        _f32_dev(pl, "lse_p")
+    if outs is None:
+        outs = [(torch.empty_like(o), torch.empty_like(lse)) for _ in parts]
+    n = len(parts)
+    P = ctypes.c_void_p
+    arr = lambda ts: (P * n)(*[t.data_ptr() for t in ts])
+    _check(lib().cpattn_merge_backward(n, arr([p[0] for p in parts]), arr([p[1] for p in parts]), rows, d,
+                                       o.data_ptr(), lse.data_ptr(), g_o.data_ptr(),
+                                       None if g_lse is None else g_lse.data_ptr(),
+                                       arr([x[0] for x in outs]), arr([x[1] for x in outs]), _stream(stream)))
+    return outs
+
+
+def sink_backward(o: torch.Tensor, lse: torch.Tensor, sink_logits: torch.Tensor, g_o: torch.Tensor, stream=None):
+    """Adjoints of :func:`apply_sink` from the result it left (``o`` [H, n, d]
+    and ``lse`` [H, n] after the sink) and the output gradient ``g_o``:
+    returns (dO, dLSE, d sink_logits) for the result before the sink."""
+    H, n, d = o.shape
+    if lse.shape != (H, n) or sink_logits.shape != (H,) or g_o.shape != o.shape:
+        raise ValueError("sink_backward expects o [H, n, d], lse [H, n], sink_logits [H], g_o [H, n, d]")
+    for t, name in ((o, "o"), (lse, "lse"), (sink_logits, "sink_logits"), (g_o, "g_o")):
+        _f32_dev(t, name)
+    g_in = torch.empty_like(o)
+    gl_in = torch.empty_like(lse)
+    ga = torch.empty_like(sink_logits)
+    _check(lib().cpattn_sink_backward(o.data_ptr(), lse.data_ptr(), sink_logits.data_ptr(), H, n, d,
+                                      g_o.data_ptr(), g_in.data_ptr(), gl_in.data_ptr(), ga.data_ptr(),
+                                      _stream(stream)))
+    return g_in, gl_in, ga
 
 
 def _f32_dev(t, name):

@@ -757,6 +757,92 @@ extern "C" int cpattn_apply_sink(float* o, float* lse, const float* sink_logits,
     return e == hipSuccess ? CPATTN_OK : hip_fail(e, "sink launch");
 }
 
+// threads per row for the row kernels of the merge and sink adjoints: a power
+// of two <= 64, so that a row's lanes lie in one wave
+static int32_t row_threads(int64_t d) {
+    int32_t t = 1;
+    while (t < 64 && 2 * t <= d / 4) t *= 2;
+    return t;
+}
+
+extern "C" int cpattn_merge_backward(int n_parts, const float* const* o_parts, const float* const* lse_parts,
+                                     int64_t n_rows, int64_t d, const float* o, const float* lse, const float* g_o,
+                                     const float* g_lse, float* const* g_o_parts, float* const* g_lse_parts,
+                                     void* stream) {
+    const char* who = "cpattn_merge_backward";
+    if (n_parts < 1 || n_parts > kMaxMergeParts)
+        return fail(CPATTN_EINVAL, "%s: n_parts = %d out of range [1, %d]", who, n_parts, kMaxMergeParts);
+    if (n_rows < 0 || d < 4 || d > (1 << 20)) return fail(CPATTN_EINVAL, "%s: bad sizes", who);
+    if (d % 4 != 0) return fail(CPATTN_EUNSUPPORTED, "%s: d must be a multiple of 4", who);
+    if (!o_parts || !lse_parts || !g_o_parts || !g_lse_parts) return fail(CPATTN_EINVAL, "%s: NULL part arrays", who);
+    if (n_rows == 0) return CPATTN_OK;
+    if (!o || !lse || !g_o) return fail(CPATTN_EINVAL, "%s: NULL pointer", who);
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    MergeBwdArgs a{};
+    bool aligned = al16(o) && al16(g_o);
+    for (int p = 0; p < n_parts; ++p) {
+        if (!o_parts[p] || !lse_parts[p] || !g_o_parts[p] || !g_lse_parts[p])
+            return fail(CPATTN_EINVAL, "%s: part %d has a NULL pointer", who, p);
+        aligned = aligned && al16(o_parts[p]) && al16(g_o_parts[p]);
+        a.o[p] = o_parts[p];
+        a.l[p] = lse_parts[p];
+        a.go[p] = g_o_parts[p];
+        a.gl[p] = g_lse_parts[p];
+    }
+    if (!aligned) return fail(CPATTN_EUNSUPPORTED, "%s: O arrays must be 16-byte aligned", who);
+    a.o_m = o;
+    a.l_m = lse;
+    a.g = g_o;
+    a.g_l = g_lse;
+    a.rows = n_rows;
+    a.n = n_parts;
+    a.d = (int32_t)d;
+    a.tpr = row_threads(d);
+    const int64_t rows_per_block = 256 / a.tpr;
+    const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many rows", who);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(merge_backward_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "merge backward launch");
+}
+
+extern "C" int cpattn_sink_backward(const float* o, const float* lse, const float* sink_logits, int64_t n_heads,
+                                    int64_t n_rows, int64_t d, const float* g_o, float* g_o_in, float* g_lse_in,
+                                    float* g_sink, void* stream) {
+    const char* who = "cpattn_sink_backward";
+    if (n_heads < 1 || n_rows < 0 || d < 4 || d > (1 << 20)) return fail(CPATTN_EINVAL, "%s: bad sizes", who);
+    if (d % 4 != 0) return fail(CPATTN_EUNSUPPORTED, "%s: d must be a multiple of 4", who);
+    if (n_heads > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many heads", who);
+    if (!sink_logits || !g_sink) return fail(CPATTN_EINVAL, "%s: NULL pointer", who);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (n_rows > 0) {
+        if (!o || !lse || !g_o || !g_o_in || !g_lse_in) return fail(CPATTN_EINVAL, "%s: NULL pointer", who);
+        auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+        if (!al16(o) || !al16(g_o) || !al16(g_o_in))
+            return fail(CPATTN_EUNSUPPORTED, "%s: O arrays must be 16-byte aligned", who);
+        SinkBwdArgs a{};
+        a.y = o;
+        a.lse = lse;
+        a.sink = sink_logits;
+        a.g = g_o;
+        a.go = g_o_in;
+        a.gl = g_lse_in;
+        a.rows = n_heads * n_rows;
+        a.rows_per_head = n_rows;
+        a.d = (int32_t)d;
+        a.tpr = row_threads(d);
+        const int64_t rows_per_block = 256 / a.tpr;
+        const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+        if (blocks > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many rows", who);
+        hipLaunchKernelGGL(sink_backward_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    }
+    // with no rows the sink gradient is zero (the reduction over nothing)
+    hipLaunchKernelGGL(sink_grad_kernel, dim3((unsigned)n_heads), dim3(256), 0, st, g_lse_in, n_rows, g_sink);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "sink backward launch");
+}
+
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------

@@ -130,4 +130,128 @@ __global__ void __launch_bounds__(256) sink_kernel(const SinkArgs a) {
     if (t == 0) a.lse[row] = lt;
 }
 
+// ---------------------------------------------------------------------------
+// Adjoints of the merge ("Context Parallelism in ART", section 04): for the
+// merged (O, L) of parts (O_p, L_p), w_p = exp(L_p - L), an output gradient G
+// and an optional LSE gradient gL,
+//     dO_p = w_p G,   dL_p = w_p (dot(G, O_p - O) + gL).
+// A part with L_p = -inf (or a row with L = -inf) gets w_p = 0.  One row per
+// `tpr` consecutive lanes of one wave (tpr a power of two <= 64, d % 4 == 0),
+// the dot products reduced with lane shuffles.  HBM-bound: per row reads
+// (n + 2) d + n + 2 floats and writes n (d + 1).
+struct MergeBwdArgs {
+    const float* o[kMaxMergeParts];
+    const float* l[kMaxMergeParts];
+    float* go[kMaxMergeParts];
+    float* gl[kMaxMergeParts];
+    const float* o_m;      // merged O
+    const float* l_m;      // merged L
+    const float* g;        // gradient of merged O
+    const float* g_l;      // gradient of merged L, or null
+    int64_t rows;
+    int32_t n;
+    int32_t d;
+    int32_t tpr;
+};
+
+__device__ __forceinline__ float row_sum(float v, int tpr) {
+    for (int off = tpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__global__ void __launch_bounds__(256) merge_backward_kernel(const MergeBwdArgs a) {
+    const int rows_per_block = 256 / a.tpr;
+    const int sub = threadIdx.x / a.tpr;
+    const int t = threadIdx.x % a.tpr;
+    const int64_t row = (int64_t)blockIdx.x * rows_per_block + sub;
+    // rows past the end still take part in the shuffles (with zeros)
+    const bool active = row < a.rows;
+    const int chunks = a.d / 4;
+    const float L = active ? a.l_m[row] : -INFINITY;
+    const float gL = active && a.g_l ? a.g_l[row] : 0.f;
+    const float4* om = reinterpret_cast<const float4*>(a.o_m + row * a.d);
+    const float4* gg = reinterpret_cast<const float4*>(a.g + row * a.d);
+    for (int p = 0; p < a.n; ++p) {
+        const float lp = active ? a.l[p][row] : -INFINITY;
+        const float w = (L == -INFINITY || lp == -INFINITY) ? 0.f : expf(lp - L);
+        const float4* op = reinterpret_cast<const float4*>(a.o[p] + row * a.d);
+        float4* gop = reinterpret_cast<float4*>(a.go[p] + row * a.d);
+        float dot = 0.f;
+        if (active) {
+            for (int c = t; c < chunks; c += a.tpr) {
+                const float4 gv = gg[c], ov = op[c], mv = om[c];
+                dot += gv.x * (ov.x - mv.x) + gv.y * (ov.y - mv.y) + gv.z * (ov.z - mv.z) + gv.w * (ov.w - mv.w);
+                gop[c] = float4{w * gv.x, w * gv.y, w * gv.z, w * gv.w};
+            }
+        }
+        dot = row_sum(dot, a.tpr);
+        if (active && t == 0) a.gl[p][row] = w * (dot + gL);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Adjoints of the sink step (section 06), from the buffers cpattn_apply_sink
+// leaves: y = w O and L' = logaddexp(L, a_h), with u = exp(a_h - L') the
+// sink's share of the softmax mass and w = 1 - u:
+//     dO = w G,   dL = u dot(G, y),   da_h = -sum over the head's rows of u dot(G, y)
+// (the same values as w (1 - w) dot(G, O) with O before the sink).  A row with
+// no visible key (L = -inf: L' = a_h, y = 0) gets dO = 0, dL = 0.  The row
+// terms are written to dL; sink_grad_kernel then sums them per head in a
+// fixed order (deterministic).
+struct SinkBwdArgs {
+    const float* y;
+    const float* lse;      // L'
+    const float* sink;     // [heads]
+    const float* g;
+    float* go;
+    float* gl;
+    int64_t rows;
+    int64_t rows_per_head;
+    int32_t d;
+    int32_t tpr;
+};
+
+__global__ void __launch_bounds__(256) sink_backward_kernel(const SinkBwdArgs a) {
+    const int rows_per_block = 256 / a.tpr;
+    const int sub = threadIdx.x / a.tpr;
+    const int t = threadIdx.x % a.tpr;
+    const int64_t row = (int64_t)blockIdx.x * rows_per_block + sub;
+    const bool active = row < a.rows;
+    float u = 1.f;
+    if (active) {
+        const float lt = a.lse[row];
+        const float s = a.sink[row / a.rows_per_head];
+        u = lt == -INFINITY ? 1.f : fminf(1.f, expf(s - lt));
+    }
+    const float w = 1.f - u;
+    const float4* yv = reinterpret_cast<const float4*>(a.y + row * a.d);
+    const float4* gv = reinterpret_cast<const float4*>(a.g + row * a.d);
+    float4* gov = reinterpret_cast<float4*>(a.go + row * a.d);
+    float dot = 0.f;
+    if (active) {
+        for (int c = t; c < a.d / 4; c += a.tpr) {
+            const float4 gg = gv[c], yy = yv[c];
+            dot += gg.x * yy.x + gg.y * yy.y + gg.z * yy.z + gg.w * yy.w;
+            gov[c] = float4{w * gg.x, w * gg.y, w * gg.z, w * gg.w};
+        }
+    }
+    dot = row_sum(dot, a.tpr);
+    if (active && t == 0) a.gl[row] = u * dot;
+}
+
+// g_sink[h] = -sum_r gl[h][r]; one workgroup per head, fixed reduction order
+__global__ void __launch_bounds__(256) sink_grad_kernel(const float* gl, int64_t rows_per_head, float* g_sink) {
+    __shared__ float part[256];
+    const int h = blockIdx.x;
+    float acc = 0.f;
+    for (int64_t r = threadIdx.x; r < rows_per_head; r += 256) acc += gl[h * rows_per_head + r];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if ((int)threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) g_sink[h] = -part[0];
+}
+
 }  // namespace cpattn

@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 6
+#define CPATTN_VERSION_MINOR 7
 
 typedef enum {
     CPATTN_OK = 0,
@@ -264,6 +264,35 @@ int cpattn_ring_backward(int N, const cpattn_tensor* q_blocks, const cpattn_tens
                          float scale, const float* const* lse, const float* const* delta,
                          const cpattn_tensor* dout_blocks, float* const* dq, float* const* dk, float* const* dv,
                          void* stream);
+
+/* Adjoints of cpattn_merge ("Context Parallelism in ART", section 04): for
+ * the merged result (o, lse) of parts (o_p, lse_p), w_p = exp(lse_p - lse),
+ * an output gradient g_o and an optional LSE gradient g_lse (NULL: zero),
+ *   g_o_parts[p]   = w_p g_o,
+ *   g_lse_parts[p] = w_p (dot(g_o, o_p - o) + g_lse).
+ * A part with lse_p = -inf (or a row with lse = -inf) gets w_p = 0.  Rows of
+ * d fp32 values, as in cpattn_merge: o_parts, lse_parts, g_o_parts and
+ * g_lse_parts are HOST arrays of n_parts device pointers; o, g_o and every O
+ * array 16-byte aligned, d % 4 == 0 (else EUNSUPPORTED).  Outputs are written
+ * (not added).  1 <= n_parts <= 64. */
+int cpattn_merge_backward(int n_parts, const float* const* o_parts, const float* const* lse_parts,
+                          int64_t n_rows, int64_t d, const float* o, const float* lse, const float* g_o,
+                          const float* g_lse, float* const* g_o_parts, float* const* g_lse_parts, void* stream);
+
+/* Adjoints of cpattn_apply_sink (same page, section 06), from the buffers it
+ * leaves: o = y = w O and lse = L' = logaddexp(L, a_h), where O, L are the
+ * result before the sink.  With u = exp(a_h - L') (the sink's share of the
+ * softmax mass) and w = 1 - u, for an output gradient g_o:
+ *   g_o_in  = w g_o                              (gradient of O)
+ *   g_lse_in = u dot(g_o, y)   = w (1 - w) dot(g_o, O)   (gradient of L)
+ *   g_sink[h] = -sum over the head's rows of g_lse_in
+ * (L' itself is taken as unused downstream).  o, g_o, g_o_in: [n_heads]
+ * [n_rows][d] fp32, 16-byte aligned, d % 4 == 0; lse, g_lse_in: [n_heads]
+ * [n_rows]; sink_logits, g_sink: [n_heads]; all device memory, outputs
+ * written.  The per-head sum runs in a fixed order (deterministic). */
+int cpattn_sink_backward(const float* o, const float* lse, const float* sink_logits, int64_t n_heads,
+                         int64_t n_rows, int64_t d, const float* g_o, float* g_o_in, float* g_lse_in,
+                         float* g_sink, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* cpattn_last_error(void);

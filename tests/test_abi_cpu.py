@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_error_string(L):
     import context_blockwise_attention_amd as cp
-    assert cp.version() == (0, 6)
+    assert cp.version() == (0, 7)
     assert isinstance(L.cpattn_last_error(), bytes)
 
 
@@ -141,3 +141,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(cp, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         cp.lib()
+
+
+def test_merge_and_sink_backward_validation(L):
+    P = ctypes.c_void_p
+    parts = (P * 65)(*([0x1000] * 65))
+    bad = (P * 2)(0x1000, 0x1004)
+    a = (0x2000, 0x3000, 0x4000)   # o, lse, g_o
+    assert L.cpattn_merge_backward(0, parts, parts, 10, 128, *a, None, parts, parts, None) == EINVAL
+    assert L.cpattn_merge_backward(65, parts, parts, 10, 128, *a, None, parts, parts, None) == EINVAL
+    assert L.cpattn_merge_backward(2, parts, parts, 10, 0, *a, None, parts, parts, None) == EINVAL
+    assert L.cpattn_merge_backward(2, parts, parts, 10, 6, *a, None, parts, parts, None) == EUNSUPPORTED
+    assert L.cpattn_merge_backward(2, parts, parts, 10, 128, *a, None, None, parts, None) == EINVAL
+    assert L.cpattn_merge_backward(2, parts, parts, 0, 128, *a, None, parts, parts, None) == OK     # no rows
+    assert L.cpattn_merge_backward(2, bad, parts, 10, 128, *a, None, parts, parts, None) == EUNSUPPORTED
+    assert L.cpattn_merge_backward(2, parts, parts, 10, 128, 0, 0x3000, 0x4000, None, parts, parts, None) == EINVAL
+    assert L.cpattn_last_error().startswith(b"cpattn_merge_backward")
+    s = (0x2000, 0x3000, 0x5000)   # o, lse, sink
+    assert L.cpattn_sink_backward(*s, 0, 10, 128, 0x4000, 0x6000, 0x7000, 0x8000, None) == EINVAL
+    assert L.cpattn_sink_backward(*s, 2, 10, 6, 0x4000, 0x6000, 0x7000, 0x8000, None) == EUNSUPPORTED
+    assert L.cpattn_sink_backward(0x2000, 0x3000, 0, 2, 10, 128, 0x4000, 0x6000, 0x7000, 0x8000, None) == EINVAL
+    assert L.cpattn_sink_backward(*s, 2, 10, 128, 0x4000, 0x6004, 0x7000, 0x8000, None) == EUNSUPPORTED
+    assert L.cpattn_sink_backward(*s, 2, 10, 128, 0x4000, 0x6000, 0, 0x8000, None) == EINVAL
+    assert L.cpattn_last_error().startswith(b"cpattn_sink_backward")
