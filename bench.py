@@ -36,15 +36,19 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_bf16_pp_kernel_tree64k.json")
-KERNEL_NAME = "attn_bf16_pp_kernel<128, 64, 2>"
+KERNEL_NAME = "attn_bf16_pp_kernel<128, 64, 2, false>"   # as the profiler names it (no window)
+
+
+KERNEL_SOURCES = ("attn_kernel.hpp", "attn_bf16_kernel.hpp")   # the bf16 forward kernel's device code
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources; a traffic record is only used while it matches."""
+    """Hash of the forward kernel's HIP sources; a traffic record is only used
+    while it matches."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "context_blockwise_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -67,6 +71,8 @@ def traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mi
     w = _pmc_per_dispatch(write_csv, KERNEL_NAME, "WRITE_SIZE")
     cf = _pmc_per_dispatch(copy_fetch_csv, "", "FETCH_SIZE")
     cw = _pmc_per_dispatch(copy_write_csv, "", "WRITE_SIZE")
+    if len(f) < launches_per_step or len(w) < launches_per_step or not cf or not cw:
+        raise SystemExit("traffic: no %s dispatches (or no copy) in the counter files" % KERNEL_NAME)
     copy_bytes = copy_mib * 2 ** 20
     # the copy kernel is the largest dispatch of the calibration run
     k_fetch = copy_bytes / (max(cf) * 1024.0)
@@ -282,7 +288,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample: query rows per head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing (diagnostic runs)")
-    ap.add_argument("--no-balance", action="store_true", help="skip the contiguous vs zig-zag ring comparison")
+    ap.add_argument("--no-balance", action="store_true",
+                    help="skip the extra legs (zig-zag comparison, GQA, window, backward)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="calibration run: only time a plain device copy of this many MiB")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
