@@ -36,17 +36,19 @@ struct BwdTileBf16 {
 };
 
 // Physical chunk of logical chunk c in row r (row within a tile) is
-// c ^ bwd_swizzle(r).  Row reads: the 8 rows that 8 consecutive lanes read
-// (r32 0-7 -> rows 0-3, 8-11 in the permuted order; likewise per 16 lanes)
-// get distinct swizzles.  Transposed reads: a 16-lane group reads rows
-// 8g + kq (kq 0-3) at chunks base ^ t (t 0-1), and swizzle >> 1 differs
-// between those rows, so the 8 (row, t) chunks are distinct.  For 64-column
-// rows two rows share one 256-byte bank window, so the swizzle is spread over
-// row pairs instead.
+// c ^ bwd_swizzle(r).  A 16-byte row read serves 16 lanes per pass, here 16
+// different rows (rows 0-15 or 16-31 in the permuted MFMA order), so the
+// swizzle is a permutation of 0-15 over any 16 consecutive rows.  A
+// transposed read (ds_read_b64_tr_b16) serves 32 lanes: rows 8g + kq
+// (kq = 0-3) at chunks (4b + 2 G2 + t) ^ swizzle with G2, t in {0, 1}, so the
+// swizzles of those four rows must differ above bit 1; then the 32 lanes'
+// 8-byte words fall in 16 distinct chunks x 2 halves.  With 128-byte rows (d
+// 64) two rows share a 256-byte bank line: the same conditions then hold for
+// the even and the odd rows separately, over 8 chunks.
 template <int D>
 __device__ __forceinline__ int bwd_swizzle(int r) {
-    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Per-lane offsets of one wave's share of a tile's direct loads: load i of
@@ -420,25 +422,38 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
     // B operand rows of dP: this wave's 32 V rows (tile `wave` of the V block) in natural order
     const BwdRowRead vread{SM::V_OFF + wave * TT::BYTES + r32 * TT::ROWB, g ^ bwd_swizzle<D>(r32)};
 
-    auto issue = [&](int step, int slot) {
-        const int hq = step / n_tiles;
-        const int q0 = i_begin + (step - hq * n_tiles) * BM;
-        const int head = kvh * J.kv_group + hq;
-        const __bf16* qh = reinterpret_cast<const __bf16*>(J.q) + head * J.q_sh;
-        const __bf16* doh = reinterpret_cast<const __bf16*>(J.dout) + head * J.do_sh;
-        dma_q.issue(sgpr_rsrc(qh, (J.n_q - 1) * q_st * 2 + D * 2), q0, q_st, wave, lds + SM::Q_OFF + slot * TT::BYTES);
-        dma_do.issue(sgpr_rsrc(doh, (J.n_q - 1) * do_st * 2 + D * 2), q0, do_st, wave,
+    // (query head, tile) of the next load and of the tile being computed,
+    // advanced without divisions; the job's fields are read once
+    const int kv_group = J.kv_group, n_q = J.n_q;
+    const __bf16* const q_all = reinterpret_cast<const __bf16*>(J.q);
+    const __bf16* const do_all = reinterpret_cast<const __bf16*>(J.dout);
+    const int64_t q_sh = J.q_sh, do_sh = J.do_sh;
+    const float* const lse_all = J.lse;
+    const float* const delta_all = J.delta;
+    int ld_head = kvh * kv_group, ld_tile = 0;
+    auto issue = [&](int slot) {
+        const int q0 = i_begin + ld_tile * BM;
+        const __bf16* qh = q_all + ld_head * q_sh;
+        const __bf16* doh = do_all + ld_head * do_sh;
+        dma_q.issue(sgpr_rsrc(qh, (n_q - 1) * q_st * 2 + D * 2), q0, q_st, wave, lds + SM::Q_OFF + slot * TT::BYTES);
+        dma_do.issue(sgpr_rsrc(doh, (n_q - 1) * do_st * 2 + D * 2), q0, do_st, wave,
                      lds + SM::DO_OFF + slot * TT::BYTES);
         if (wave == 0)
-            dma_b32(sgpr_rsrc(J.lse + (int64_t)head * J.n_q, J.n_q * 4), (q0 + lane) * 4,
+            dma_b32(sgpr_rsrc(lse_all + (int64_t)ld_head * n_q, n_q * 4), (q0 + lane) * 4,
                     lds_addr(lds + SM::L_OFF + slot * 256));
         else if (wave == 1)
-            dma_b32(sgpr_rsrc(J.delta + (int64_t)head * J.n_q, J.n_q * 4), (q0 + lane) * 4,
+            dma_b32(sgpr_rsrc(delta_all + (int64_t)ld_head * n_q, n_q * 4), (q0 + lane) * 4,
                     lds_addr(lds + SM::DL_OFF + slot * 256));
+        if (++ld_tile == n_tiles) {
+            ld_tile = 0;
+            ++ld_head;
+        }
     };
 
     const float c2 = args.scale_log2;
-    if (steps > 0) issue(0, 0);
+    if (steps > 0) issue(0);
+    const int qbase = J.qbase, qstride = J.qstride;
+    int cur_tile = 0;
     for (int step = 0; step < steps; ++step) {
         const int slot = step & 1;
         // this wave's loads of the current tile (and, first, the V block)
@@ -446,8 +461,9 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         // is free
         __builtin_amdgcn_s_waitcnt(0xF70);
         bwd_tile_barrier();
-        if (step + 1 < steps) issue(step + 1, slot ^ 1);
-        const int q0 = i_begin + (step % n_tiles) * BM;
+        if (step + 1 < steps) issue(slot ^ 1);
+        const int q0 = i_begin + cur_tile * BM;
+        if (++cur_tile == n_tiles) cur_tile = 0;
         const lds_byte* qt = lds + SM::Q_OFF + slot * TT::BYTES;
         const lds_byte* dt = lds + SM::DO_OFF + slot * TT::BYTES;
 
@@ -461,8 +477,8 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         // lane (key jk, half g), value i: query row q0 + il, il = 16 (i / 8) + 8 g + i % 8
         const auto* lp = reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + SM::L_OFF + slot * 256) + 8 * g;
         const auto* dlp = reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + SM::DL_OFF + slot * 256) + 8 * g;
-        const int yq0 = J.qbase + J.qstride * q0;
-        const int yq1 = J.qbase + J.qstride * min(q0 + BM - 1, J.n_q - 1);
+        const int yq0 = qbase + qstride * q0;
+        const int yq1 = qbase + qstride * min(q0 + BM - 1, n_q - 1);
         const bool full = yq0 >= kmax && (!tree || yq1 < hmin);
         bf16x8 pb[2], dsb[2];
         // a row without gradient (LSE = -inf) gets p = 0
@@ -484,8 +500,8 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
             for (int i = 0; i < 16; ++i) {
                 const int il = (i >> 3) * 16 + (i & 7);
                 const int qrow = q0 + il + 8 * g;
-                const int y = J.qbase + J.qstride * qrow;
-                const bool vis = qrow < J.n_q && kpos <= y && y < horizon;
+                const int y = qbase + qstride * qrow;
+                const bool vis = qrow < n_q && kpos <= y && y < horizon;
                 const float p = vis ? prob(i, il) : 0.f;
                 pb[i >> 3][i & 7] = (__bf16)p;
                 dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dlp[il]));
