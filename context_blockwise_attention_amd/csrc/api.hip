@@ -846,16 +846,25 @@ extern "C" int cpattn_sink_backward(const float* o, const float* lse, const floa
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool WIN>
 static int launch_bwd_t(BwdArgs& a, bool dkv, hipStream_t st) {
     using S = BwdStage<T, D>;
-    constexpr bool bf16 = sizeof(T) == 2;
-    const int smem_dq = bf16 ? BwdDqBf16Smem<D>::BYTES : (2 * S::ROW_ELEMS + S::T_ELEMS) * (int)sizeof(T) + kBwdTile * 4;
-    const int smem_dkv =
-        bf16 ? BwdDkvBf16Smem<D>::BYTES : (2 * S::ROW_ELEMS + 2 * S::T_ELEMS) * (int)sizeof(T) + 2 * kBwdTile * 4;
-    // bf16: tiles loaded straight into LDS, transposed operands read with ds_read_b64_tr_b16
-    const auto kq = bf16 ? attn_bwd_dq_bf16_kernel<D> : attn_bwd_dq_kernel<T, D>;
-    const auto kkv = bf16 ? attn_bwd_dkv_bf16_kernel<D> : attn_bwd_dkv_kernel<T, D>;
+    // bf16: tiles loaded straight into LDS, transposed operands read with
+    // ds_read_b64_tr_b16; fp32: register-staged tiles
+    void (*kq)(BwdArgs);
+    void (*kkv)(BwdArgs);
+    int smem_dq, smem_dkv;
+    if constexpr (sizeof(T) == 2) {
+        kq = attn_bwd_dq_bf16_kernel<D, WIN>;
+        kkv = attn_bwd_dkv_bf16_kernel<D, WIN>;
+        smem_dq = BwdDqBf16Smem<D, WIN ? 1 : kBwdDqKeyTile / kBwdTile>::BYTES;
+        smem_dkv = BwdDkvBf16Smem<D>::BYTES;
+    } else {
+        kq = attn_bwd_dq_kernel<T, D, WIN>;
+        kkv = attn_bwd_dkv_kernel<T, D, WIN>;
+        smem_dq = (2 * S::ROW_ELEMS + S::T_ELEMS) * (int)sizeof(T) + 2 * kBwdTile * 4;
+        smem_dkv = (2 * S::ROW_ELEMS + 2 * S::T_ELEMS) * (int)sizeof(T) + 3 * kBwdTile * 4;
+    }
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kq),
@@ -873,9 +882,15 @@ static int launch_bwd_t(BwdArgs& a, bool dkv, hipStream_t st) {
     return e == hipSuccess ? CPATTN_OK : hip_fail(e, "backward launch");
 }
 
+template <bool WIN>
+static int launch_bwd_w(BwdArgs& a, bool dkv, int dtype, int d, hipStream_t st) {
+    if (dtype == CPATTN_BF16)
+        return d == 128 ? launch_bwd_t<__bf16, 128, WIN>(a, dkv, st) : launch_bwd_t<__bf16, 64, WIN>(a, dkv, st);
+    return d == 128 ? launch_bwd_t<float, 128, WIN>(a, dkv, st) : launch_bwd_t<float, 64, WIN>(a, dkv, st);
+}
+
 static int launch_bwd(BwdArgs& a, bool dkv, int dtype, int d, hipStream_t st) {
-    if (dtype == CPATTN_BF16) return d == 128 ? launch_bwd_t<__bf16, 128>(a, dkv, st) : launch_bwd_t<__bf16, 64>(a, dkv, st);
-    return d == 128 ? launch_bwd_t<float, 128>(a, dkv, st) : launch_bwd_t<float, 64>(a, dkv, st);
+    return a.mask.window > 0 ? launch_bwd_w<true>(a, dkv, dtype, d, st) : launch_bwd_w<false>(a, dkv, dtype, d, st);
 }
 
 struct BwdPair {
@@ -949,7 +964,6 @@ static int check_bwd_common(const cpattn_tensor* q, const cpattn_tensor* dout, c
                             const float* lse, const float* delta, const char* who) {
     int rc;
     if (!mask) return fail(CPATTN_EINVAL, "%s: mask is NULL", who);
-    if (mask->window > 0) return fail(CPATTN_EUNSUPPORTED, "%s: the backward does not support sliding windows", who);
     if ((rc = check_tensor(dout, who, "dout"))) return rc;
     if (dout->dtype != q->dtype || dout->d != q->d || dout->n_heads != q->n_heads || dout->n_tok != q->n_tok)
         return fail(CPATTN_EINVAL, "%s: dout must match q in dtype, heads, tokens and head dim", who);

@@ -129,24 +129,30 @@ __device__ __forceinline__ void bwd_tile_barrier() {
 // on the 64K tree ring, at 256 registers)
 // ---------------------------------------------------------------------------
 constexpr int kBwdDqKeyTile = 64;
-template <int D>
+template <int D, int KT_ = kBwdDqKeyTile / kBwdTile>
 struct BwdDqBf16Smem {
     using TT = BwdTileBf16<D>;
-    static constexpr int KT = kBwdDqKeyTile / kBwdTile;     // 32-row sub-tiles per key tile
+    static constexpr int KT = KT_;     // 32-row sub-tiles per key tile
     static constexpr int SLOT = KT * TT::BYTES;
     static constexpr int K_OFF = 0;
     static constexpr int V_OFF = 2 * SLOT;
     static constexpr int E_OFF = 4 * SLOT;   // two 256-byte horizon slots (64-lane loads)
-    static constexpr int BYTES = E_OFF + 2 * 256;
+    static constexpr int L_OFF = E_OFF + 2 * 256;   // window on a tree: the keys' logical positions
+    static constexpr int BYTES = L_OFF + 2 * 256;
 };
 
-template <int D>
+// WIN: sliding window on logical positions (the forward's rule): causal ->
+// a lowest visible key index per query; tree -> the query's logical position
+// against each key's, staged beside the horizons.  The tile walk skips and
+// classifies tiles with the window (TileCursor<BN, true>).  Windowed runs use
+// 32-key tiles (the window's registers do not fit beside two sub-tiles).
+template <int D, bool WIN>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_bf16_kernel(const BwdArgs args) {
     using TT = BwdTileBf16<D>;
-    using SM = BwdDqBf16Smem<D>;
-    constexpr int BN = kBwdDqKeyTile;
+    using SM = BwdDqBf16Smem<D, WIN ? 1 : kBwdDqKeyTile / kBwdTile>;
     constexpr int KT = SM::KT;
+    constexpr int BN = KT * kBwdTile;
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
     int ji, head, qtile;
@@ -194,11 +200,21 @@ attn_bwd_dq_bf16_kernel(const BwdArgs args) {
     const float dlt = valid_q ? J.delta[(int64_t)head * J.n_q + qi] : 0.f;
     const float c2 = args.scale_log2;
     const int jlim = min(J.n_k - 1, ypos < J.kbase ? -1 : (ypos - J.kbase) / J.kstride);
+    int jlo = 0, ly = 0;
+    if (WIN) {
+        if (tree) {
+            ly = valid_q ? args.mask.lpos[ypos] : 0;
+        } else {
+            const int lowest = ypos - args.mask.window + 1 - J.kbase;   // lowest visible key position, block-relative
+            jlo = lowest <= 0 ? 0 : (lowest + J.kstride - 1) / J.kstride;
+        }
+    }
 
     lds_byte* const lds = to_lds(smem);
     const i32x4 k_rsrc = sgpr_rsrc(kh, (J.n_k - 1) * k_st * 2 + D * 2);
     const i32x4 v_rsrc = sgpr_rsrc(vh, (J.n_k - 1) * v_st * 2 + D * 2);
     const i32x4 e_rsrc = sgpr_rsrc(args.mask.end, args.mask.n_pos * 4);
+    const i32x4 l_rsrc = WIN ? sgpr_rsrc(args.mask.lpos, args.mask.n_pos * 4) : i32x4{};
     BwdDma<D> dk, dv;
     dk.init(wave, lane, k_st);
     dv.init(wave, lane, v_st);
@@ -212,13 +228,15 @@ attn_bwd_dq_bf16_kernel(const BwdArgs args) {
         }
         if (tree && wave == 0)
             dma_b32(e_rsrc, (kblk.kbase + kblk.kstride * (tile * BN + lane)) * 4, lds_addr(lds + SM::E_OFF + slot * 256));
+        if (WIN && tree && wave == 1)
+            dma_b32(l_rsrc, (kblk.kbase + kblk.kstride * (tile * BN + lane)) * 4, lds_addr(lds + SM::L_OFF + slot * 256));
     };
 
     f32x16 acc[TT::DBLK];
 #pragma unroll
     for (int b = 0; b < TT::DBLK; ++b) acc[b] = f32x16{};
 
-    TileCursor<BN> cur;
+    TileCursor<BN, WIN> cur;
     cur.init(kblk, args.mask, y0, y1);
     int t_cur, f_cur, t_nxt = 0, f_nxt = 0;
     if (cur.next(kblk, args.mask, y1, &t_cur, &f_cur)) {
@@ -262,14 +280,17 @@ attn_bwd_dq_bf16_kernel(const BwdArgs args) {
                     }
             } else {
                 const int lim = jlim - t_cur * BN - 8 * g;
+                const int lo = jlo - t_cur * BN - 8 * g;   // window (causal)
                 const auto* ep = reinterpret_cast<const __attribute__((address_space(3))) int*>(lds + SM::E_OFF + slot * 256) + 8 * g;
+                const auto* lkp = reinterpret_cast<const __attribute__((address_space(3))) int*>(lds + SM::L_OFF + slot * 256) + 8 * g;
 #pragma unroll
                 for (int h = 0; h < KT; ++h)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int jl = 32 * h + (i >> 3) * 16 + (i & 7);   // + 8 g, folded into lim and ep
+                        const int jl = 32 * h + (i >> 3) * 16 + (i & 7);   // + 8 g, folded into lim, lo, ep, lkp
                         bool vis = jl <= lim;
                         if (tree) vis = vis && ypos < ep[jl];
+                        if (WIN) vis = vis && (tree ? ly - lkp[jl] < args.mask.window : jl >= lo);
                         const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[h][i], c2, -lse2)) : 0.f;
                         dsb[2 * h + (i >> 3)][i & 7] = (__bf16)(p * (dp[h][i] - dlt));
                     }
@@ -325,11 +346,16 @@ struct BwdDkvBf16Smem {
     static constexpr int DO_OFF = Q_OFF + 2 * TT::BYTES;  // two slots
     static constexpr int L_OFF = DO_OFF + 2 * TT::BYTES;  // LSE, two 256-byte slots (64-lane loads)
     static constexpr int DL_OFF = L_OFF + 2 * 256;        // D, two slots
-    static constexpr int R_OFF = DL_OFF + 2 * 256;        // per-wave reductions
+    static constexpr int LQ_OFF = DL_OFF + 2 * 256;       // window on a tree: the queries' logical positions
+    static constexpr int R_OFF = LQ_OFF + 2 * 256;        // per-wave reductions
     static constexpr int BYTES = R_OFF + 64;
 };
 
-template <int D>
+// WIN: sliding window on logical positions.  Every tile takes the masked
+// path (query and key also within the window: ly - lk < window, logical =
+// physical for a causal mask); with a causal mask the query range ends at the
+// last key's position + window, with a tree it is not narrowed.
+template <int D, bool WIN>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
     using TT = BwdTileBf16<D>;
@@ -407,9 +433,13 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         return (int)min<int64_t>(i, J.n_q);
     };
     const int i_begin = first_query_at_or_after(pos_lo) / BM * BM;
-    const int i_end = hmax == (int)0x80000000 ? 0 : first_query_at_or_after((int64_t)hmax);   // exclusive
+    int i_end = hmax == (int)0x80000000 ? 0 : first_query_at_or_after((int64_t)hmax);   // exclusive
+    if (WIN && !tree && kmax != (int)0x80000000)
+        i_end = min(i_end, first_query_at_or_after((int64_t)kmax + args.mask.window));
     const int n_tiles = i_end > i_begin ? (i_end - i_begin + BM - 1) / BM : 0;
     const int steps = n_tiles * J.kv_group;   // (query head, tile) pairs, head-major
+    // this lane's key's logical position
+    const int lk = !WIN || !valid_k ? 0 : tree ? args.mask.lpos[kpos] : kpos;
 
     f32x16 acck[TT::DBLK], accv[TT::DBLK];
 #pragma unroll
@@ -422,6 +452,7 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
     // B operand rows of dP: this wave's 32 V rows (tile `wave` of the V block) in natural order
     const BwdRowRead vread{SM::V_OFF + wave * TT::BYTES + r32 * TT::ROWB, g ^ bwd_swizzle<D>(r32)};
 
+    const int qbase = J.qbase, qstride = J.qstride;
     // (query head, tile) of the next load and of the tile being computed,
     // advanced without divisions; the job's fields are read once
     const int kv_group = J.kv_group, n_q = J.n_q;
@@ -444,6 +475,9 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         else if (wave == 1)
             dma_b32(sgpr_rsrc(delta_all + (int64_t)ld_head * n_q, n_q * 4), (q0 + lane) * 4,
                     lds_addr(lds + SM::DL_OFF + slot * 256));
+        else if (WIN && tree && wave == 2)
+            dma_b32(sgpr_rsrc(args.mask.lpos, args.mask.n_pos * 4), (qbase + qstride * (q0 + lane)) * 4,
+                    lds_addr(lds + SM::LQ_OFF + slot * 256));
         if (++ld_tile == n_tiles) {
             ld_tile = 0;
             ++ld_head;
@@ -452,7 +486,6 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
 
     const float c2 = args.scale_log2;
     if (steps > 0) issue(0);
-    const int qbase = J.qbase, qstride = J.qstride;
     int cur_tile = 0;
     for (int step = 0; step < steps; ++step) {
         const int slot = step & 1;
@@ -479,7 +512,8 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         const auto* dlp = reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + SM::DL_OFF + slot * 256) + 8 * g;
         const int yq0 = qbase + qstride * q0;
         const int yq1 = qbase + qstride * min(q0 + BM - 1, n_q - 1);
-        const bool full = yq0 >= kmax && (!tree || yq1 < hmin);
+        const bool full = !WIN && yq0 >= kmax && (!tree || yq1 < hmin);
+        const auto* lqp = reinterpret_cast<const __attribute__((address_space(3))) int*>(lds + SM::LQ_OFF + slot * 256) + 8 * g;
         bf16x8 pb[2], dsb[2];
         // a row without gradient (LSE = -inf) gets p = 0
         auto prob = [&](int i, int il) {
@@ -501,7 +535,8 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
                 const int il = (i >> 3) * 16 + (i & 7);
                 const int qrow = q0 + il + 8 * g;
                 const int y = qbase + qstride * qrow;
-                const bool vis = qrow < n_q && kpos <= y && y < horizon;
+                bool vis = qrow < n_q && kpos <= y && y < horizon;
+                if (WIN) vis = vis && (tree ? lqp[il] : y) - lk < args.mask.window;
                 const float p = vis ? prob(i, il) : 0.f;
                 pb[i >> 3][i & 7] = (__bf16)p;
                 dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dlp[il]));

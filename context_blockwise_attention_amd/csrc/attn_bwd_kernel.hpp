@@ -6,7 +6,8 @@
 //     p_j = exp(s_j - L),   dS_j = p_j (dot(g, v_j) - D),
 //     dV_j += p_j g,   dQ += scale dS_j k_j,   dK_j += scale dS_j q,
 // with the complete L and D, so a stage's backward needs no other stage and
-// the stages' contributions add.  Two kernels:
+// the stages' contributions add.  Two kernels (the fp32 path; bf16 inputs
+// use the kernels of attn_bwd_bf16_kernel.hpp):
 //
 //  * attn_bwd_dq_kernel: a workgroup owns 128 query rows (4 waves x 32) and
 //    walks the key tiles they see exactly like the forward kernel
@@ -165,7 +166,10 @@ __device__ __forceinline__ int mfma_row_perm(int r32) {
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// WIN: sliding window on logical positions, as in the forward (causal: a
+// lowest visible key index per query; tree: logical positions compared, the
+// keys' staged beside their horizons)
+template <typename T, int D, bool WIN>
 __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dq_kernel(const BwdArgs args) {
     using E = Elem<T>;
     using S = BwdStage<T, D>;
@@ -220,6 +224,15 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dq_kernel(const BwdArgs 
     const bool live = lse > -INFINITY;   // a row with no visible key has no gradient
     const float c2 = args.scale_log2;
     const int kperm = mfma_row_perm(r32);
+    int jlo = 0, ly = 0;
+    if (WIN) {
+        if (tree) {
+            ly = valid_q ? args.mask.lpos[ypos] : 0;
+        } else {
+            const int lowest = ypos - args.mask.window + 1 - J.kbase;
+            jlo = lowest <= 0 ? 0 : (lowest + J.kstride - 1) / J.kstride;
+        }
+    }
 
     f32x16 acc[DBLK];
 #pragma unroll
@@ -228,13 +241,13 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dq_kernel(const BwdArgs 
     T* Ks = reinterpret_cast<T*>(smem);
     T* Kt = Ks + S::ROW_ELEMS;
     T* Vs = Kt + S::T_ELEMS;
-    int* Es = reinterpret_cast<int*>(Vs + S::ROW_ELEMS);
+    int* Es = reinterpret_cast<int*>(Vs + S::ROW_ELEMS);   // horizons, then (window) logical positions
 
     // staging: K (rows and transposed) and V (rows) of a 32-key tile; group
     // gi < GROUPS is K, the next GROUPS are V
     constexpr int GPT = (2 * S::GROUPS + kBwdThreads - 1) / kBwdThreads;
     u32x4 sreg[GPT][4];
-    int endreg = 0;
+    int endreg = 0, lreg = 0;
     auto stage_load = [&](int tile) {
 #pragma unroll
         for (int x = 0; x < GPT; ++x) {
@@ -246,6 +259,10 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dq_kernel(const BwdArgs 
             const int j = tile * BN + tid;
             endreg = j < J.n_k ? args.mask.end[J.kbase + J.kstride * j] : (int)0x80000000;
         }
+        if (WIN && tree && tid >= BN && tid < 2 * BN) {
+            const int j = tile * BN + tid - BN;
+            lreg = j < J.n_k ? args.mask.lpos[J.kbase + J.kstride * j] : 0;
+        }
     };
     auto stage_store = [&]() {
 #pragma unroll
@@ -255,10 +272,11 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dq_kernel(const BwdArgs 
             else if (gi < 2 * S::GROUPS) bwd_store_group<T, D>(gi - S::GROUPS, sreg[x], Vs, nullptr);
         }
         if (tree && tid < BN) Es[tid] = endreg;
+        if (WIN && tree && tid >= BN && tid < 2 * BN) Es[tid] = lreg;   // Ls = Es + BN
     };
 
     const int jlim = min(J.n_k - 1, ypos < J.kbase ? -1 : (ypos - J.kbase) / J.kstride);
-    TileCursor<BN> cur;
+    TileCursor<BN, WIN> cur;
     cur.init(kblk, args.mask, y0, y1);
     int tile, full;
     bool have = cur.next(kblk, args.mask, y1, &tile, &full);
@@ -287,6 +305,7 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dq_kernel(const BwdArgs 
             if (!full) {
                 vis = vis && tile * BN + jl <= jlim;
                 if (tree) vis = vis && ypos < Es[jl];
+                if (WIN) vis = vis && (tree ? ly - Es[BN + jl] < args.mask.window : tile * BN + jl >= jlo);
             }
             const float p = vis ? __builtin_amdgcn_exp2f(s[i] * c2 - lse2) : 0.f;
             dsb[i >> 3][i & 7] = (T)(p * (dp[i] - dlt));
@@ -320,7 +339,10 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dq_kernel(const BwdArgs 
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// WIN: sliding window on logical positions; the queries' logical positions
+// are staged with their LSE and D (tree), and with a causal mask the query
+// range ends at the last key's position + window.
+template <typename T, int D, bool WIN>
 __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs args) {
     using E = Elem<T>;
     using S = BwdStage<T, D>;
@@ -377,7 +399,19 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs
         return (int)min<int64_t>(i, J.n_q);
     };
     const int i_begin = first_query_at_or_after(pos_lo) / BM * BM;
-    const int i_end = hmax == (int)0x80000000 ? 0 : first_query_at_or_after((int64_t)hmax);   // exclusive
+    int i_end = hmax == (int)0x80000000 ? 0 : first_query_at_or_after((int64_t)hmax);   // exclusive
+    if (WIN && !tree) {
+        // the workgroup's last key position + window bounds the queries that can see it
+        int kl = valid_k ? kpos : (int)0x80000000;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) kl = max(kl, __shfl_xor(kl, off));
+        if (lane == 0) s_hmax[wave] = kl;
+        __syncthreads();
+        kl = max(max(s_hmax[0], s_hmax[1]), max(s_hmax[2], s_hmax[3]));
+        __syncthreads();
+        if (kl != (int)0x80000000) i_end = min(i_end, first_query_at_or_after((int64_t)kl + args.mask.window));
+    }
+    const int lk = !WIN || !valid_k ? 0 : tree ? args.mask.lpos[kpos] : kpos;
 
     f32x16 acck[DBLK], accv[DBLK];
 #pragma unroll
@@ -392,6 +426,7 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs
     T* Dt = Ds_ + S::ROW_ELEMS;        // dO transposed
     float* L2s = reinterpret_cast<float*>(Dt + S::T_ELEMS);
     float* Dls = L2s + BM;
+    int* Lqs = reinterpret_cast<int*>(Dls + BM);   // window on a tree: the queries' logical positions
 
     const float c2 = args.scale_log2;
     const int qperm = mfma_row_perm(r32);
@@ -407,6 +442,7 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs
         const float* delta = J.delta + (int64_t)head * J.n_q;
         u32x4 sreg[GPT][4];
         float lreg = 0.f, dreg = 0.f;
+        int lqreg = 0;
         auto stage_load = [&](int q0) {
 #pragma unroll
             for (int x = 0; x < GPT; ++x) {
@@ -418,6 +454,7 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs
                 const int i = q0 + tid;
                 lreg = i < J.n_q ? lse[i] : -INFINITY;
                 dreg = i < J.n_q ? delta[i] : 0.f;
+                if (WIN && tree) lqreg = i < J.n_q ? args.mask.lpos[J.qbase + J.qstride * i] : 0;
             }
         };
         auto stage_store = [&]() {
@@ -430,6 +467,7 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs
             if (tid < BM) {
                 L2s[tid] = lreg * 1.4426950408889634f;
                 Dls[tid] = dreg;
+                if (WIN && tree) Lqs[tid] = lqreg;
             }
         };
         if (i_begin < i_end) stage_load(i_begin);
@@ -455,7 +493,8 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs
                 const int qrow_i = q0 + il;
                 const int y = J.qbase + J.qstride * qrow_i;
                 const float l2 = L2s[il];
-                const bool vis = qrow_i < J.n_q && kpos <= y && y < horizon && l2 > -INFINITY;
+                bool vis = qrow_i < J.n_q && kpos <= y && y < horizon && l2 > -INFINITY;
+                if (WIN) vis = vis && (tree ? Lqs[il] : y) - lk < args.mask.window;
                 const float p = vis ? __builtin_amdgcn_exp2f(s[i] * c2 - l2) : 0.f;
                 pb[i >> 3][i & 7] = (T)p;
                 dsb[i >> 3][i & 7] = (T)(p * (dp[i] - Dls[il]));

@@ -232,7 +232,8 @@ int cpattn_apply_sink(float* o, float* lse, const float* sink_logits, int64_t n_
  * key j of any stage: p_j = exp(s_j - L), dS_j = p_j (dot(g, v_j) - D),
  * dV_j += p_j g, dQ += scale dS_j k_j, dK_j += scale dS_j q.  A stage needs
  * only its own key block plus the query's L and D, and the stages'
- * contributions add.  Sliding-window descriptors are EUNSUPPORTED here. */
+ * contributions add.  Sliding-window descriptors apply their window here as in
+ * the forward (a key outside a query's window gets no gradient from it). */
 
 /* delta[h][i] = dot(dout[h][i][:], o[h][i][:]) for a complete output o
  * (fp32 [H][n][d], contiguous) and output gradient dout (bf16 or fp32, same

@@ -12,6 +12,8 @@ of each gradient (P and dS are rounded to bf16 for the MFMAs, a relative
   sizes and offsets, every element of dQ, dK, dV;
 * grouped-query K/V (8 query heads over 2);
 * ring backward of a packed tree (N = 4), every element;
+* sliding windows on logical positions: causal partials (windows 1 .. past
+  the block, ragged offsets), a packed tree, and the ring of a packed tree;
 * the 64K tree ring at full size: the output gradient is nonzero on 256
   sampled rows per head only, so dK and dV of every key come from those rows
   (checked on every key) and dQ on those rows.
@@ -75,6 +77,79 @@ def test_partial_backward(cp, dtype, d, maskname, nq, nk, qbase, kbase):
     _check("dq", dq, rq, dtype)
     _check("dk", dk, rk, dtype)
     _check("dv", dv, rv, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window", [1, 37, 300])
+@pytest.mark.parametrize("nq,nk,qbase,kbase", [(300, 300, 0, 0), (200, 333, 150, 100)])
+def test_partial_backward_causal_window(cp, dtype, d, window, nq, nk, qbase, kbase):
+    H = 2
+    q, _, _ = workloads.qkv(61, H, nq, d, dtype)
+    _, k, v = workloads.qkv(62, H, nk, d, dtype)
+    G = _grad_out(63, H, nq, d, dtype)
+    mask = cp.Mask.causal(max(qbase + nq, kbase + nk)).with_window(window)
+    omask = oracle.Causal(window=window)
+    qpos, kpos = qbase + np.arange(nq), kbase + np.arange(nk)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    o, l = cp.partial(qd, kd, vd, mask, (qbase, 1), (kbase, 1))
+    delta = cp.backward_delta(o, gd)
+    dq, dk, dv = cp.partial_backward(qd, kd, vd, mask, l, delta, gd, (qbase, 1), (kbase, 1))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q, k, v, qpos, kpos, omask)
+    rq, rk, rv = oracle.attention_backward(q, k, v, qpos, kpos, O, L, G.double().numpy(), omask)
+    _check("dq", dq, rq, dtype)
+    _check("dk", dk, rk, dtype)
+    _check("dv", dv, rv, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("window", [3, 90, 250])
+def test_partial_backward_tree_window(cp, dtype, window):
+    H, d = 2, 128
+    seg, parent = workloads.tree_prompt_completions(160, (96, 64, 80))
+    n = len(seg)
+    q, k, v = workloads.qkv(64, H, n, d, dtype)
+    G = _grad_out(65, H, n, d, dtype)
+    mask = cp.Mask.tree(seg, parent).with_window(window)
+    omask = oracle.Tree(seg, parent, window=window)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    o, l = cp.partial(qd, kd, vd, mask)
+    delta = cp.backward_delta(o, gd)
+    dq, dk, dv = cp.partial_backward(qd, kd, vd, mask, l, delta, gd)
+    torch.cuda.synchronize()
+    pos = np.arange(n)
+    O, L = oracle.attention(q, k, v, pos, pos, omask)
+    rq, rk, rv = oracle.attention_backward(q, k, v, pos, pos, O, L, G.double().numpy(), omask)
+    _check("dq", dq, rq, dtype)
+    _check("dk", dk, rk, dtype)
+    _check("dv", dv, rv, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ring_backward_tree_window(cp, dtype):
+    N, H, d, window = 4, 2, 128, 150
+    seg, parent = workloads.tree_prompt_completions(384, (128, 200, 96, 160))
+    n = len(seg) // N * N
+    seg = seg[:n]
+    c = n // N
+    q, k, v = workloads.qkv(66, H, n, d, dtype)
+    G = _grad_out(67, H, n, d, dtype)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    mask = cp.Mask.tree(seg, parent).with_window(window)
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    pos = [(r * c, 1) for r in range(N)]
+    out = cp.ring_emulate(blk(qd), blk(kd), blk(vd), pos, mask)
+    deltas = [cp.backward_delta(out[r][0], blk(gd)[r].contiguous()) for r in range(N)]
+    grads = cp.ring_backward(blk(qd), blk(kd), blk(vd), pos, mask, [out[r][1] for r in range(N)], deltas, blk(gd))
+    torch.cuda.synchronize()
+    allpos = np.arange(n)
+    omask = oracle.Tree(seg, parent, window=window)
+    O, L = oracle.attention(q, k, v, allpos, allpos, omask)
+    rq, rk, rv = oracle.attention_backward(q, k, v, allpos, allpos, O, L, G.double().numpy(), omask)
+    for name, i, ref in (("dq", 0, rq), ("dk", 1, rk), ("dv", 2, rv)):
+        got = torch.cat([grads[r][i] for r in range(N)], 1)
+        _check(name, got, ref, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
