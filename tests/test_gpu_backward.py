@@ -14,6 +14,8 @@ of each gradient (P and dS are rounded to bf16 for the MFMAs, a relative
 * ring backward of a packed tree (N = 4), every element;
 * sliding windows on logical positions: causal partials (windows 1 .. past
   the block, ragged offsets), a packed tree, and the ring of a packed tree;
+* striped position maps (stride 4), with and without a window, every pair of
+  stripes against the complete forward's (O, L);
 * the 64K tree ring at full size: the output gradient is nonzero on 256
   sampled rows per head only, so dK and dV of every key come from those rows
   (checked on every key) and dQ on those rows.
@@ -150,6 +152,37 @@ def test_ring_backward_tree_window(cp, dtype):
     for name, i, ref in (("dq", 0, rq), ("dk", 1, rk), ("dv", 2, rv)):
         got = torch.cat([grads[r][i] for r in range(N)], 1)
         _check(name, got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("window", [0, 45])
+def test_partial_backward_striped(cp, dtype, window):
+    """Striped layout (global position P idx + r): every (query stripe, key
+    stripe) pair, strides > 1 in both position maps."""
+    H, n, d, P = 2, 150, 128, 4
+    q, k, v = workloads.qkv(68, H, n * P, d, dtype)
+    G = _grad_out(69, H, n * P, d, dtype)
+    lay = workloads.striped(n * P, P)
+    mask = cp.Mask.causal(n * P)
+    if window:
+        mask = mask.with_window(window)
+    omask = oracle.Causal(window=window)
+    for a in (0, 3):
+        for b in range(P):
+            qq, gg = q[:, lay[a]].contiguous(), G[:, lay[a]].contiguous()
+            kk, vv = k[:, lay[b]].contiguous(), v[:, lay[b]].contiguous()
+            qd, kd, vd, gd = qq.cuda(), kk.cuda(), vv.cuda(), gg.cuda()
+            # the complete forward of the stripe's queries (all key stripes), then this pair's gradients
+            O, L = oracle.attention(qq, k, v, lay[a], np.arange(n * P), omask)
+            ot = torch.from_numpy(O.astype(np.float32)).cuda()
+            lt = torch.from_numpy(L.astype(np.float32)).cuda()
+            delta = cp.backward_delta(ot, gd)
+            dq, dk, dv = cp.partial_backward(qd, kd, vd, mask, lt, delta, gd, (a, P), (b, P))
+            torch.cuda.synchronize()
+            rq, rk, rv = oracle.attention_backward(qq, kk, vv, lay[a], lay[b], O, L, gg.double().numpy(), omask)
+            _check("dq %d/%d" % (a, b), dq, rq, dtype)
+            _check("dk %d/%d" % (a, b), dk, rk, dtype)
+            _check("dv %d/%d" % (a, b), dv, rv, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
