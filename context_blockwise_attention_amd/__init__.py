@@ -89,11 +89,14 @@ def lib():
                                                                                P]
         L.cpattn_ring_backward.argtypes = [ctypes.c_int, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P]
         L.cpattn_merge_backward.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int64, P, P, P, P, P, P, P]
+        L.cpattn_ring_backward_chunks.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_float, P, P, P,
+                                                  P, P, P, P]
         L.cpattn_sink_backward.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P, P, P]
         for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
                   "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan",
                   "cpattn_apply_sink", "cpattn_mask_with_window", "cpattn_backward_delta",
-                  "cpattn_partial_backward", "cpattn_ring_backward", "cpattn_merge_backward",
+                  "cpattn_partial_backward", "cpattn_ring_backward", "cpattn_ring_backward_chunks",
+                  "cpattn_merge_backward",
                   "cpattn_sink_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -366,6 +369,37 @@ def apply_sink(o: torch.Tensor, lse: torch.Tensor, sink_logits: torch.Tensor, st
     _check(lib().cpattn_apply_sink(o.data_ptr(), lse.data_ptr(), sink_logits.data_ptr(), H, n, d,
                                    _stream(stream)))
     return o, lse
+
+
+def ring_backward_chunks(q_chunks, k_chunks, v_chunks, pos, mask: Mask, lses, deltas, douts,
+                         chunks_per_rank: int, scale=None, grads=None, stream=None):
+    """Backward of :func:`ring_emulate_chunks` (all ranks): C =
+    ``chunks_per_rank`` chunks per rank, chunk c of rank r at index r*C + c.
+    ``grads[i]`` = (dq, dk, dv) fp32 per chunk (zero-filled new tensors if
+    None); returns it."""
+    NC = len(q_chunks)
+    C = int(chunks_per_rank)
+    if C < 1 or NC % C:
+        raise ValueError("the number of chunks must be a multiple of chunks_per_rank")
+    n_ranks = NC // C
+    d = q_chunks[0].shape[2]
+    if grads is None:
+        grads = [(torch.zeros(q_chunks[i].shape, dtype=torch.float32, device=q_chunks[i].device),
+                  torch.zeros(k_chunks[i].shape, dtype=torch.float32, device=k_chunks[i].device),
+                  torch.zeros(v_chunks[i].shape, dtype=torch.float32, device=v_chunks[i].device)) for i in range(NC)]
+    qd = (_Tensor * NC)(*[_desc(t, "q") for t in q_chunks])
+    kd = (_Tensor * NC)(*[_desc(t, "k") for t in k_chunks])
+    vd = (_Tensor * NC)(*[_desc(t, "v") for t in v_chunks])
+    od = (_Tensor * NC)(*[_desc(t, "dout") for t in douts])
+    pd = (_PosMap * NC)(*[_posmap(p) for p in pos])
+    P = ctypes.c_void_p
+    arr = lambda ts, name: (P * NC)(*[_f32_dev(t, name) for t in ts])
+    _check(lib().cpattn_ring_backward_chunks(n_ranks, C, qd, kd, vd, pd, mask.handle,
+                                             float(_default_scale(d) if scale is None else scale),
+                                             arr(lses, "lse"), arr(deltas, "delta"), od,
+                                             arr([g[0] for g in grads], "dq"), arr([g[1] for g in grads], "dk"),
+                                             arr([g[2] for g in grads], "dv"), _stream(stream)))
+    return grads
 
 
 def merge_backward(parts, merged, g_o, g_lse=None, outs=None, stream=None):

@@ -900,12 +900,15 @@ struct BwdPair {
     float *dq, *dk, *dv;
 };
 
-// One dQ launch and one dK/dV launch for a set of pairs; the pairs of one
-// call must not share a query block (dQ) or a key block (dK/dV).
-static int run_bwd(const std::vector<BwdPair>& pairs, const cpattn_mask* m, float scale, hipStream_t st) {
+// One dQ launch and one dK/dV launch for a set of pairs (`which`: 1 = dQ
+// only, 2 = dK/dV only, 3 = both); the pairs of one call must not share a
+// query block (dQ) or a key block (dK/dV).
+static int run_bwd(const std::vector<BwdPair>& pairs, const cpattn_mask* m, float scale, hipStream_t st,
+                   int which = 3) {
     for (size_t first = 0; first < pairs.size(); first += kMaxJobs) {
         const size_t n = std::min<size_t>(kMaxJobs, pairs.size() - first);
         for (int dkv = 0; dkv < 2; ++dkv) {
+            if (!(which & (1 << dkv))) continue;
             BwdArgs a{};
             a.mask = mask_args(m);
             a.scale = scale;
@@ -1009,6 +1012,74 @@ extern "C" int cpattn_partial_backward(const cpattn_tensor* q, const cpattn_tens
     if (!pair_nonempty(mask, q_pos, q->n_tok, k_pos, k->n_tok)) return CPATTN_OK;
     std::vector<BwdPair> pairs{BwdPair{q, k, v, dout, q_pos, k_pos, lse, delta, dq, dk, dv}};
     return run_bwd(pairs, mask, scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int cpattn_ring_backward_chunks(int N, int C, const cpattn_tensor* q_chunks,
+                                           const cpattn_tensor* k_chunks, const cpattn_tensor* v_chunks,
+                                           const cpattn_posmap* pos, const cpattn_mask* mask, float scale,
+                                           const float* const* lse, const float* const* delta,
+                                           const cpattn_tensor* dout_chunks, float* const* dq, float* const* dk,
+                                           float* const* dv, void* stream) {
+    const char* who = "cpattn_ring_backward_chunks";
+    int rc;
+    if (N < 1 || N > 64) return fail(CPATTN_EINVAL, "%s: N = %d out of range [1, 64]", who, N);
+    if (C < 1 || C > 8) return fail(CPATTN_EINVAL, "%s: C = %d out of range [1, 8]", who, C);
+    if (!q_chunks || !k_chunks || !v_chunks || !pos || !lse || !delta || !dout_chunks || !dq || !dk || !dv)
+        return fail(CPATTN_EINVAL, "%s: NULL array argument", who);
+    if ((rc = check_scale(scale, who))) return rc;
+    const int NC = N * C;
+    for (int i = 0; i < NC; ++i) {
+        if ((rc = check_qkv(&q_chunks[i], &k_chunks[i], &v_chunks[i], who))) return rc;
+        if ((rc = check_bwd_common(&q_chunks[i], &dout_chunks[i], mask, lse[i], delta[i], who))) return rc;
+        if (q_chunks[i].n_tok != k_chunks[i].n_tok)
+            return fail(CPATTN_EINVAL, "%s: chunk %d holds %lld queries but %lld keys", who, i,
+                        (long long)q_chunks[i].n_tok, (long long)k_chunks[i].n_tok);
+        if (q_chunks[i].dtype != q_chunks[0].dtype || q_chunks[i].d != q_chunks[0].d ||
+            q_chunks[i].n_heads != q_chunks[0].n_heads || k_chunks[i].n_heads != k_chunks[0].n_heads)
+            return fail(CPATTN_EUNSUPPORTED, "%s: every chunk must share dtype, head dim and heads", who);
+        if ((rc = check_posmap(pos[i], k_chunks[i].n_tok, mask, who, "pos"))) return rc;
+        if (q_chunks[i].n_tok > 0 &&
+            ((rc = check_out(dq[i], lse[i], who)) || (rc = check_out(dk[i], delta[i], who)) ||
+             (rc = check_out(dv[i], delta[i], who))))
+            return rc;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    auto pair = [&](int qi, int ki) {
+        return BwdPair{&q_chunks[qi], &k_chunks[ki], &v_chunks[ki], &dout_chunks[qi], pos[qi], pos[ki], lse[qi],
+                       delta[qi], dq[qi], dk[ki], dv[ki]};
+    };
+    // Round k: every chunk a of rank r meets every key chunk c of rank
+    // b = (r - k) mod N.  A launch may hold one pair per query chunk (dQ)
+    // and, separately, one per key chunk (dK/dV): the dQ launches of a round
+    // take one key chunk index c at a time (query chunks (r, a) all differ),
+    // the dK/dV launches one query chunk index a (key chunks (b, c) all differ).
+    for (int k = 0; k < N; ++k) {
+        for (int c = 0; c < C; ++c) {
+            std::vector<BwdPair> pairs;
+            for (int r = 0; r < N; ++r) {
+                const int b = ((r - k) % N + N) % N;
+                for (int a = 0; a < C; ++a) {
+                    const int qi = r * C + a, ki = b * C + c;
+                    if (pair_nonempty(mask, pos[qi], q_chunks[qi].n_tok, pos[ki], k_chunks[ki].n_tok))
+                        pairs.push_back(pair(qi, ki));
+                }
+            }
+            if ((rc = run_bwd(pairs, mask, scale, st, 1))) return rc;
+        }
+        for (int a = 0; a < C; ++a) {
+            std::vector<BwdPair> pairs;
+            for (int r = 0; r < N; ++r) {
+                const int b = ((r - k) % N + N) % N;
+                for (int c = 0; c < C; ++c) {
+                    const int qi = r * C + a, ki = b * C + c;
+                    if (pair_nonempty(mask, pos[qi], q_chunks[qi].n_tok, pos[ki], k_chunks[ki].n_tok))
+                        pairs.push_back(pair(qi, ki));
+                }
+            }
+            if ((rc = run_bwd(pairs, mask, scale, st, 2))) return rc;
+        }
+    }
+    return CPATTN_OK;
 }
 
 extern "C" int cpattn_ring_backward(int N, const cpattn_tensor* q_blocks, const cpattn_tensor* k_blocks,

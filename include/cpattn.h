@@ -266,6 +266,20 @@ int cpattn_ring_backward(int N, const cpattn_tensor* q_blocks, const cpattn_tens
                          const cpattn_tensor* dout_blocks, float* const* dq, float* const* dk, float* const* dv,
                          void* stream);
 
+/* Backward of cpattn_ring_emulate_chunks (all N ranks, C chunks each, chunk
+ * c of rank r at index r*C + c; zig-zag: C = 2): in round k every query chunk
+ * of rank r meets every key chunk of rank (r - k) mod N; dQ stays with the
+ * query chunk, dK/dV are added to the key chunk's buffers.  Per round, C dQ
+ * launches (one per key chunk index, so no two jobs write the same dQ rows)
+ * and C dK/dV launches (one per query chunk index).  Host arrays of N*C
+ * entries as in cpattn_ring_backward.  1 <= N <= 64, 1 <= C <= 8; C = 1 is
+ * cpattn_ring_backward. */
+int cpattn_ring_backward_chunks(int N, int C, const cpattn_tensor* q_chunks, const cpattn_tensor* k_chunks,
+                                const cpattn_tensor* v_chunks, const cpattn_posmap* pos, const cpattn_mask* mask,
+                                float scale, const float* const* lse, const float* const* delta,
+                                const cpattn_tensor* dout_chunks, float* const* dq, float* const* dk,
+                                float* const* dv, void* stream);
+
 /* Adjoints of cpattn_merge ("Context Parallelism in ART", section 04): for
  * the merged result (o, lse) of parts (o_p, lse_p), w_p = exp(lse_p - lse),
  * an output gradient g_o and an optional LSE gradient g_lse (NULL: zero),

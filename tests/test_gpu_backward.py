@@ -16,6 +16,8 @@ of each gradient (P and dS are rounded to bf16 for the MFMAs, a relative
   the block, ragged offsets), a packed tree, and the ring of a packed tree;
 * striped position maps (stride 4), with and without a window, every pair of
   stripes against the complete forward's (O, L);
+* the zig-zag (chunked) ring backward (N = 4, two chunks per rank), causal
+  and packed tree, every element;
 * the 64K tree ring at full size: the output gradient is nonzero on 256
   sampled rows per head only, so dK and dV of every key come from those rows
   (checked on every key) and dQ on those rows.
@@ -231,6 +233,42 @@ def test_ring_backward_tree(cp, dtype):
     rq, rk, rv = oracle.attention_backward(q, k, v, allpos, allpos, O, L, G.double().numpy(), omask)
     for name, i, ref in (("dq", 0, rq), ("dk", 1, rk), ("dv", 2, rv)):
         got = torch.cat([grads[r][i] for r in range(N)], 1)
+        _check(name, got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("maskname", ["causal", "tree"])
+def test_zigzag_ring_backward(cp, dtype, maskname):
+    N, H, d = 4, 2, 128
+    if maskname == "causal":
+        n = 8 * 96
+        mask, omask = cp.Mask.causal(n), oracle.Causal()
+    else:
+        seg, parent = workloads.tree_prompt_completions(320, (160, 200, 88))
+        n = len(seg)
+        mask, omask = cp.Mask.tree(seg, parent), oracle.Tree(seg, parent)
+    c = n // (2 * N)
+    q, k, v = workloads.qkv(70, H, n, d, dtype)
+    G = _grad_out(71, H, n, d, dtype)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    chunks = [ch for r in range(N) for ch in (r, 2 * N - 1 - r)]
+    cut = lambda t: [t[:, ch * c:(ch + 1) * c].contiguous() for ch in chunks]
+    pos = [(ch * c, 1) for ch in chunks]
+    Q, K, V, Gs = cut(qd), cut(kd), cut(vd), cut(gd)
+    out = cp.ring_emulate_chunks(Q, K, V, pos, mask, chunks_per_rank=2)
+    deltas = [cp.backward_delta(out[i][0], Gs[i]) for i in range(2 * N)]
+    grads = cp.ring_backward_chunks(Q, K, V, pos, mask, [out[i][1] for i in range(2 * N)], deltas, Gs,
+                                    chunks_per_rank=2)
+    torch.cuda.synchronize()
+    allpos = np.arange(n)
+    O, L = oracle.attention(q[:, :2 * N * c], k[:, :2 * N * c], v[:, :2 * N * c], allpos[:2 * N * c],
+                            allpos[:2 * N * c], omask)
+    rq, rk, rv = oracle.attention_backward(q[:, :2 * N * c], k[:, :2 * N * c], v[:, :2 * N * c], allpos[:2 * N * c],
+                                           allpos[:2 * N * c], O, L, G[:, :2 * N * c].double().numpy(), omask)
+    for name, j, ref in (("dq", 0, rq), ("dk", 1, rk), ("dv", 2, rv)):
+        got = torch.zeros((H, 2 * N * c, d), dtype=torch.float64)
+        for i, ch in enumerate(chunks):
+            got[:, ch * c:(ch + 1) * c] = grads[i][j].double().cpu()
         _check(name, got, ref, dtype)
 
 
