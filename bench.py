@@ -232,11 +232,34 @@ def window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N, window: i
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the same ring's backward (10 d FLOPs per visible pair, as the headline's)
+    g = torch.Generator(device="cpu").manual_seed(8)
+    douts = [x.contiguous() for x in blk(torch.randn((H, n, d), generator=g).to(torch.bfloat16).to(dev))]
+    deltas = [torch.empty((H, c), dtype=torch.float32, device=dev) for _ in range(N)]
+    grads = [tuple(torch.zeros((H, c, d), dtype=torch.float32, device=dev) for _ in range(3)) for _ in range(N)]
+
+    def bstep():
+        for r in range(N):
+            cp.backward_delta(outs[r][0], douts[r], deltas[r], stream=stream)
+        cp.ring_backward(Q, K, V, pos, mask, [outs[r][1] for r in range(N)], deltas, douts, grads=grads,
+                         stream=stream)
+
+    bstep()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        bstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / 3
+    bflops = 2.5 * flops
     mask.free()
     return {"workload": "tree64k ring of %d, sliding window of %d logical positions" % (N, window),
             "visible_pairs_per_head": pairs, "ms_per_step": round(ms, 4),
             "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
-            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "backward": {"ms_per_step": round(bms, 4), "TFLOP/s": round(bflops / (bms * 1e-3) / 1e12, 2),
+                         "frac_of_bf16_peak": round(bflops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
 
 
 def backward_ring(cp, torch, dev, qd, kd, vd, seg, parent, N, outs, A, steps: int = 5):

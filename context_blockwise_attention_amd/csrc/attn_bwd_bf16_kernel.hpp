@@ -347,14 +347,21 @@ struct BwdDkvBf16Smem {
     static constexpr int L_OFF = DO_OFF + 2 * TT::BYTES;  // LSE, two 256-byte slots (64-lane loads)
     static constexpr int DL_OFF = L_OFF + 2 * 256;        // D, two slots
     static constexpr int LQ_OFF = DL_OFF + 2 * 256;       // window on a tree: the queries' logical positions
-    static constexpr int R_OFF = LQ_OFF + 2 * 256;        // per-wave reductions
-    static constexpr int BYTES = R_OFF + 64;
+    static constexpr int T_CAP = 1024;                    // window on a tree: query tiles that can see a key
+    static constexpr int T_OFF = LQ_OFF + 2 * 256;
+    static constexpr int R_OFF = T_OFF + T_CAP * 4;       // per-wave reductions
+    static constexpr int BYTES = R_OFF + 128;
 };
 
-// WIN: sliding window on logical positions.  Every tile takes the masked
-// path (query and key also within the window: ly - lk < window, logical =
-// physical for a causal mask); with a causal mask the query range ends at the
-// last key's position + window, with a tree it is not narrowed.
+// WIN: sliding window on logical positions (query and key also within the
+// window: ly - lk < window, logical = physical for a causal mask); a tile is
+// full only if its largest logical query position is within the window of the
+// smallest logical key position.  With a causal mask the query range ends at
+// the last key's position + window.  With a tree the subtree's runs are
+// walked: inside a run logical positions grow by one per position, so the
+// queries within the window of some key of the workgroup are a prefix of each
+// run, and only the tiles of those prefixes are visited (a list in LDS; a
+// list longer than T_CAP falls back to the whole range).
 template <int D, bool WIN>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
@@ -436,10 +443,65 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
     int i_end = hmax == (int)0x80000000 ? 0 : first_query_at_or_after((int64_t)hmax);   // exclusive
     if (WIN && !tree && kmax != (int)0x80000000)
         i_end = min(i_end, first_query_at_or_after((int64_t)kmax + args.mask.window));
-    const int n_tiles = i_end > i_begin ? (i_end - i_begin + BM - 1) / BM : 0;
-    const int steps = n_tiles * J.kv_group;   // (query head, tile) pairs, head-major
+    int n_tiles = i_end > i_begin ? (i_end - i_begin + BM - 1) / BM : 0;
     // this lane's key's logical position
     const int lk = !WIN || !valid_k ? 0 : tree ? args.mask.lpos[kpos] : kpos;
+    int* tlist = reinterpret_cast<int*>(smem + SM::T_OFF);
+    bool use_list = false;
+    const auto* segp = (const __attribute__((address_space(4))) int32_t*)args.mask.seg;
+    const auto* lposp = (const __attribute__((address_space(4))) int32_t*)args.mask.lpos;
+    // smallest logical key position of the workgroup (a tile whose largest
+    // logical query position is within the window of it needs no window mask)
+    int lkmin = 0;
+    if (WIN && tree) {
+        int lkm = valid_k ? lk : (int)0x80000000;
+        int lkn = valid_k ? lk : 0x7fffffff;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            lkm = max(lkm, __shfl_xor(lkm, off));
+            lkn = min(lkn, __shfl_xor(lkn, off));
+        }
+        if (lane == 0) {
+            red[16 + wave] = lkm;
+            red[24 + wave] = lkn;
+        }
+        __syncthreads();
+        lkm = wave_uniform(max(max(red[16], red[17]), max(red[18], red[19])));
+        lkmin = wave_uniform(min(min(red[24], red[25]), min(red[26], red[27])));
+        if (wave == 0) {
+            int cnt = 0, last = -1;
+            bool over = false;
+            int y = pos_lo;
+            while (lkm != (int)0x80000000 && y < hmax && !over) {
+                const i32x4 run = seg_entry(args.mask, segp[y]);
+                const int64_t vis_end = (int64_t)y + max(0, lkm + args.mask.window - lposp[y]);
+                const int e = (int)min((int64_t)min(run.y, hmax), vis_end);
+                if (e > y) {
+                    const int ib = first_query_at_or_after(e);
+                    for (int t = first_query_at_or_after(y) / BM * BM; t < ib; t += BM) {
+                        if (t <= last) continue;
+                        if (cnt == SM::T_CAP) {
+                            over = true;
+                            break;
+                        }
+                        if (lane == 0) tlist[cnt] = t;
+                        ++cnt;
+                        last = t;
+                    }
+                }
+                y = run.y;   // the next run in storage order
+            }
+            if (lane == 0) red[20] = over ? -1 : cnt;
+        }
+        __syncthreads();
+        const int c = wave_uniform(red[20]);
+        if (c >= 0) {
+            use_list = true;
+            n_tiles = c;
+        }
+    }
+    const int steps = n_tiles * J.kv_group;   // (query head, tile) pairs, head-major
+    auto tile_q0 = [&](int t) { return use_list ? wave_uniform(tlist[t]) : i_begin + t * BM; };
 
     f32x16 acck[TT::DBLK], accv[TT::DBLK];
 #pragma unroll
@@ -463,7 +525,7 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
     const float* const delta_all = J.delta;
     int ld_head = kvh * kv_group, ld_tile = 0;
     auto issue = [&](int slot) {
-        const int q0 = i_begin + ld_tile * BM;
+        const int q0 = tile_q0(ld_tile);
         const __bf16* qh = q_all + ld_head * q_sh;
         const __bf16* doh = do_all + ld_head * do_sh;
         dma_q.issue(sgpr_rsrc(qh, (n_q - 1) * q_st * 2 + D * 2), q0, q_st, wave, lds + SM::Q_OFF + slot * TT::BYTES);
@@ -495,7 +557,7 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         __builtin_amdgcn_s_waitcnt(0xF70);
         bwd_tile_barrier();
         if (step + 1 < steps) issue(slot ^ 1);
-        const int q0 = i_begin + cur_tile * BM;
+        const int q0 = tile_q0(cur_tile);
         if (++cur_tile == n_tiles) cur_tile = 0;
         const lds_byte* qt = lds + SM::Q_OFF + slot * TT::BYTES;
         const lds_byte* dt = lds + SM::DO_OFF + slot * TT::BYTES;
@@ -512,7 +574,10 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         const auto* dlp = reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + SM::DL_OFF + slot * 256) + 8 * g;
         const int yq0 = qbase + qstride * q0;
         const int yq1 = qbase + qstride * min(q0 + BM - 1, n_q - 1);
-        const bool full = !WIN && yq0 >= kmax && (!tree || yq1 < hmin);
+        bool full = yq0 >= kmax && (!tree || yq1 < hmin);
+        if (WIN)   // and every pair within the window
+            full = full && (tree ? segp[yq0] == segp[yq1] && lposp[yq1] - lkmin < args.mask.window
+                                 : yq1 - pos_lo < args.mask.window);
         const auto* lqp = reinterpret_cast<const __attribute__((address_space(3))) int*>(lds + SM::LQ_OFF + slot * 256) + 8 * g;
         bf16x8 pb[2], dsb[2];
         // a row without gradient (LSE = -inf) gets p = 0
