@@ -328,7 +328,7 @@ def main():
         print(json.dumps(rec))
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: runs on one GPU only; --gpus %d is not supported "
               "(the ring's ranks are emulated on one GPU)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

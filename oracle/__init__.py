@@ -19,8 +19,7 @@ What each function follows:
   attention: in round ``k`` rank ``r`` computes against the K/V block of rank
   ``(r - k) mod N`` and merges the result into its running answer.
 
-Readings of points the pages leave open are listed in the design doc; the ones that
-change results here: an empty visible set gives ``O = 0, L = -inf``; LSE is a
+Readings of points the pages leave open that change results here: an empty visible set gives ``O = 0, L = -inf``; LSE is a
 natural logarithm; bf16 inputs are widened exactly to fp64.
 """
 from __future__ import annotations

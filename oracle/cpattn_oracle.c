@@ -34,7 +34,7 @@
  *    (section 04), the merge adjoints (section 04) and the sink adjoints
  *    (section 06).
  *
- *  Readings where the pages are silent (each is also listed in the design doc):
+ *  Readings where the pages are silent:
  *  a query with no visible key gives O = 0 and L = -inf; merging with such a
  *  partial leaves the other side unchanged; merging two empty partials gives
  *  (0, -inf).
