@@ -164,3 +164,31 @@ def test_merge_and_sink_backward_validation(L):
     assert L.cpattn_sink_backward(*s, 2, 10, 128, 0x4000, 0x6004, 0x7000, 0x8000, None) == EUNSUPPORTED
     assert L.cpattn_sink_backward(*s, 2, 10, 128, 0x4000, 0x6000, 0, 0x8000, None) == EINVAL
     assert L.cpattn_last_error().startswith(b"cpattn_sink_backward")
+
+
+def test_backward_validation(L):
+    import context_blockwise_attention_amd as cp
+    P = ctypes.c_void_p
+    h = ctypes.c_void_p()
+    assert L.cpattn_mask_causal(64, ctypes.byref(h)) == OK
+    N, C = 2, 2
+    ts = (cp._Tensor * (N * C))(*[_tensor(cp) for _ in range(N * C)])
+    pos = (cp._PosMap * (N * C))(*[cp._PosMap(16 * i, 1) for i in range(N * C)])
+    ptrs = (P * (N * C))(*([0x2000] * (N * C)))
+    args = lambda n, c, t=ts, p=pos: (n, c, t, t, t, p, h, 0.1, ptrs, ptrs, t, ptrs, ptrs, ptrs, None)
+    assert L.cpattn_ring_backward_chunks(*args(0, C)) == EINVAL                      # N out of range
+    assert L.cpattn_ring_backward_chunks(*args(N, 0)) == EINVAL                      # C out of range
+    assert L.cpattn_ring_backward_chunks(*args(N, 9)) == EINVAL
+    far = (cp._PosMap * (N * C))(*[cp._PosMap(60, 1) for _ in range(N * C)])
+    assert L.cpattn_ring_backward_chunks(*args(N, C, p=far)) == EINVAL               # positions past the mask
+    bad = (cp._Tensor * (N * C))(*([_tensor(cp)] * 3 + [_tensor(cp, d=64)]))
+    assert L.cpattn_ring_backward_chunks(*args(N, C, t=bad)) == EUNSUPPORTED         # mixed head dims
+    assert L.cpattn_last_error().startswith(b"cpattn_ring_backward_chunks")
+    assert L.cpattn_ring_backward(0, ts, ts, ts, pos, h, 0.1, ptrs, ptrs, ts, ptrs, ptrs, ptrs, None) == EINVAL
+    t = _tensor(cp)
+    assert L.cpattn_partial_backward(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), None, cp._PosMap(0, 1),
+                                     cp._PosMap(0, 1), 0.1, 0x3000, 0x3000, ctypes.byref(t), 0x2000, 0x2000,
+                                     0x2000, None) == EINVAL                          # no mask
+    t7 = _tensor(cp, dtype=7)
+    assert L.cpattn_backward_delta(0x2000, ctypes.byref(t7), 0x3000, None) == EUNSUPPORTED
+    assert L.cpattn_mask_free(h) == OK
