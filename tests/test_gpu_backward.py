@@ -18,6 +18,8 @@ of each gradient (P and dS are rounded to bf16 for the MFMAs, a relative
   stripes against the complete forward's (O, L);
 * the zig-zag (chunked) ring backward (N = 4, two chunks per rank), causal
   and packed tree, every element;
+* random preorder trees (nested segments, ragged lengths), with and without
+  windows, split into unequal key/query blocks, every element;
 * the 64K tree ring at full size: the output gradient is nonzero on 256
   sampled rows per head only, so dK and dV of every key come from those rows
   (checked on every key) and dQ on those rows.
@@ -270,6 +272,42 @@ def test_zigzag_ring_backward(cp, dtype, maskname):
         for i, ch in enumerate(chunks):
             got[:, ch * c:(ch + 1) * c] = grads[i][j].double().cpu()
         _check(name, got, ref, dtype)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("window", [0, 40, 170])
+def test_random_tree_backward(cp, seed, window):
+    """Random nested trees: the query block and the key block are unequal
+    slices of the row, so tiles straddle runs and the window's run prefixes."""
+    from test_gpu_parity import _preorder_tree
+    rng = np.random.default_rng(100 + seed)
+    seg, parent = _preorder_tree(rng, int(rng.integers(3, 9)), 20, 140)
+    n = len(seg)
+    H, d, dtype = 2, 128, ("bf16" if seed % 2 == 0 else "f32")
+    q, k, v = workloads.qkv(72 + seed, H, n, d, dtype)
+    G = _grad_out(75 + seed, H, n, d, dtype)
+    mask = cp.Mask.tree(seg, parent)
+    if window:
+        mask = mask.with_window(window)
+    omask = oracle.Tree(seg, parent, window=window)
+    a, b = sorted(rng.integers(1, n, size=2).tolist())
+    qs, ks = slice(a // 2, n), slice(0, max(b, a // 2 + 1))   # queries from a/2 on, keys up to b
+    qq, gg = q[:, qs].contiguous(), G[:, qs].contiguous()
+    kk, vv = k[:, ks].contiguous(), v[:, ks].contiguous()
+    qpos, kpos = np.arange(n)[qs], np.arange(n)[ks]
+    # complete forward of the queries over every key, then this pair's gradients
+    O, L = oracle.attention(qq, k, v, qpos, np.arange(n), omask)
+    ot = torch.from_numpy(O.astype(np.float32)).cuda()
+    lt = torch.from_numpy(L.astype(np.float32)).cuda()
+    gd = gg.cuda()
+    delta = cp.backward_delta(ot, gd)
+    dq, dk, dv = cp.partial_backward(qq.cuda(), kk.cuda(), vv.cuda(), mask, lt, delta, gd, (int(qpos[0]), 1),
+                                     (int(kpos[0]), 1))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(qq, kk, vv, qpos, kpos, O, L, gg.double().numpy(), omask)
+    _check("dq", dq, rq, dtype)
+    _check("dk", dk, rk, dtype)
+    _check("dv", dv, rv, dtype)
 
 
 def test_tree64k_ring_backward_sampled(cp):
