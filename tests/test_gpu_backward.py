@@ -20,6 +20,8 @@ of each gradient (P and dS are rounded to bf16 for the MFMAs, a relative
   and packed tree, every element;
 * random preorder trees (nested segments, ragged lengths), with and without
   windows, split into unequal key/query blocks, every element;
+* a windowed prompt with 80 completions, whose key blocks see more query
+  tiles than the dK/dV kernel's list holds (the whole-range walk);
 * the 64K tree ring at full size: the output gradient is nonzero on 256
   sampled rows per head only, so dK and dV of every key come from those rows
   (checked on every key) and dQ on those rows.
@@ -305,6 +307,30 @@ def test_random_tree_backward(cp, seed, window):
                                      (int(kpos[0]), 1))
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_backward(qq, kk, vv, qpos, kpos, O, L, gg.double().numpy(), omask)
+    _check("dq", dq, rq, dtype)
+    _check("dk", dk, rk, dtype)
+    _check("dv", dv, rv, dtype)
+
+
+def test_window_tree_many_runs_backward(cp):
+    """A prompt with 80 short completions and a window that reaches into all
+    of them: the prompt's key blocks see more query tiles than the dK/dV
+    kernel lists, so they take its whole-range walk."""
+    H, d, dtype, window = 1, 64, "f32", 1000
+    seg, parent = workloads.tree_prompt_completions(512, (500,) * 80)
+    n = len(seg)
+    q, k, v = workloads.qkv(78, H, n, d, dtype)
+    G = _grad_out(79, H, n, d, dtype)
+    mask = cp.Mask.tree(seg, parent).with_window(window)
+    omask = oracle.Tree(seg, parent, window=window)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    o, l = cp.partial(qd, kd, vd, mask)
+    delta = cp.backward_delta(o, gd)
+    dq, dk, dv = cp.partial_backward(qd, kd, vd, mask, l, delta, gd)
+    torch.cuda.synchronize()
+    pos = np.arange(n)
+    O, L = oracle.attention(q, k, v, pos, pos, omask)
+    rq, rk, rv = oracle.attention_backward(q, k, v, pos, pos, O, L, G.double().numpy(), omask)
     _check("dq", dq, rq, dtype)
     _check("dk", dk, rk, dtype)
     _check("dv", dv, rv, dtype)
