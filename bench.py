@@ -127,6 +127,35 @@ def block_pair_counts(seg: np.ndarray, parent: np.ndarray, c: int, N: int) -> np
     return out
 
 
+def computed_tiles(seg: np.ndarray, parent: np.ndarray, c: int, bm: int = 256, bn: int = 64) -> int:
+    """Tiles (bm query rows x bn keys) the partial kernel executes for one
+    head over the whole ring of blocks of c positions: for each query tile,
+    every key tile inside a K/V block that holds a key visible to some row of
+    the query tile (own-segment prefix up to the tile's last row in that
+    segment, and every ancestor run).  Block and tile boundaries are assumed
+    aligned (c % bm == c % bn == 0)."""
+    assert c % bm == 0 and c % bn == 0
+    n, n_seg = len(seg), len(parent)
+    first = np.flatnonzero(np.r_[True, seg[1:] != seg[:-1]])
+    starts = np.zeros(n_seg, dtype=np.int64)
+    ends = np.zeros(n_seg, dtype=np.int64)
+    starts[seg[first]] = first
+    ends[seg[first]] = np.r_[first[1:], n]
+    total = 0
+    for y0 in range(0, n, bm):
+        hit = np.zeros(n // bn, dtype=bool)
+        rows = seg[y0:y0 + bm]
+        for s in np.unique(rows):
+            y_last = y0 + int(np.flatnonzero(rows == s)[-1])
+            hit[starts[s] // bn: y_last // bn + 1] = True
+            p = parent[s]
+            while p >= 0:
+                hit[starts[p] // bn: (ends[p] - 1) // bn + 1] = True
+                p = parent[p]
+        total += int(hit.sum())
+    return total
+
+
 def load_balance(cp, workloads, torch, dev, reps: int = 2):
     """Causal ring of 8 ranks over 32768 tokens (32 heads, d 128, bf16),
     contiguous blocks vs the zig-zag layout: every (rank, round) partial timed
@@ -302,6 +331,29 @@ def backward_ring(cp, torch, dev, qd, kd, vd, seg, parent, N, outs, A, steps: in
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def ring_sizes(cp, torch, dev, qd, kd, vd, mask, seg, parent, flops, sizes=(1, 8), steps: int = 10):
+    """The same row as rings of other sizes (one block of 65536; eight of
+    8192): forward ring step time and visible-pair TFLOP/s."""
+    H, n, d = qd.shape
+    stream = torch.cuda.current_stream()
+    out = {}
+    for N in sizes:
+        c = n // N
+        Q = [qd[:, r * c:(r + 1) * c] for r in range(N)]
+        K = [kd[:, r * c:(r + 1) * c] for r in range(N)]
+        V = [vd[:, r * c:(r + 1) * c] for r in range(N)]
+        pos = [(r * c, 1) for r in range(N)]
+        outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
+                    torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
+        ms = _time_reps(torch, stream, steps, lambda: cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream))
+        launches = int((block_pair_counts(seg, parent, c, N) > 0).sum(axis=1).max())
+        out["N%d" % N] = {"blocks": N, "block_tokens": c, "launches": launches, "ms_per_step": round(ms, 4),
+                          "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+                          "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del outs
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,7 +364,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample: query rows per head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing (diagnostic runs)")
     ap.add_argument("--no-balance", action="store_true",
-                    help="skip the extra legs (zig-zag comparison, GQA, window, backward)")
+                    help="skip the extra legs (ring sizes, zig-zag comparison, GQA, window, backward)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="calibration run: only time a plain device copy of this many MiB")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -378,6 +430,7 @@ def main():
     A = int(tree_visible_pairs(seg, parent, np.arange(n)).sum())
     assert A == P * (P + 1) // 2 + sum(ci * P + ci * (ci + 1) // 2 for ci in C)
     flops = 4.0 * d * H * A
+    tiles_run = computed_tiles(seg, parent, c)
 
     def step():
         cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
@@ -457,6 +510,14 @@ def main():
             "launches_per_step": launches, "avg_launch_ms": round(avg_launch_ms, 4),
             "visible_flops_per_launch": flops / launches,
         },
+        # mask waste apart from kernel efficiency: every pair of the executed
+        # (256 query x 64 key) tiles, masked ones included, at 4 d FLOPs
+        "computed_tiles": {
+            "tile": [256, 64], "tiles_per_head": tiles_run,
+            "visible_fraction": round(A / (tiles_run * 256 * 64), 5),
+            "TFLOP/s": round(tflops * tiles_run * 256 * 64 / A, 2),
+            "frac": round(tflops * tiles_run * 256 * 64 / A / PEAK_BF16_TFLOPS, 4),
+        },
         "merge": {"kernel": "merge_kernel", "parts": N, "rows": H * c, "d": d, "ms": round(merge_ms, 4),
                   "bytes": merge_bytes, "GB/s": round(merge_gbs, 1),
                   "frac_of_hbm_peak": round(merge_gbs / PEAK_HBM_GBS, 4)},
@@ -464,6 +525,7 @@ def main():
 
     if not args.no_balance:
         result["load_balance"] = load_balance(cp, workloads, torch, dev)
+        result["ring_sizes"] = ring_sizes(cp, torch, dev, qd, kd, vd, mask, seg, parent, flops)
         result["gqa"] = gqa_ring(cp, workloads, torch, dev, seg, parent, N, flops)
         result["window"] = window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N)
         result["backward"] = backward_ring(cp, torch, dev, qd, kd, vd, seg, parent, N, outs, A)
