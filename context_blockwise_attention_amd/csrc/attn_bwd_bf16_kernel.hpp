@@ -361,7 +361,11 @@ struct BwdDkvBf16Smem {
 // walked: inside a run logical positions grow by one per position, so the
 // queries within the window of some key of the workgroup are a prefix of each
 // run, and only the tiles of those prefixes are visited (a list in LDS; a
-// list longer than T_CAP falls back to the whole range).
+// list longer than T_CAP falls back to the whole range).  A list entry is the
+// tile's first query, with bit 31 set when the tile lies inside one run and
+// its last logical query position is within the window of the smallest
+// logical key position (decided from the run's bounds while the list is
+// built, so the tile loop reads no positions from memory to decide it).
 template <int D, bool WIN>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
@@ -478,13 +482,19 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
                 const int e = (int)min((int64_t)min(run.y, hmax), vis_end);
                 if (e > y) {
                     const int ib = first_query_at_or_after(e);
+                    // logical position of a query of this run: lposp[y] + (position - y)
+                    const int ly0 = lposp[y];
                     for (int t = first_query_at_or_after(y) / BM * BM; t < ib; t += BM) {
                         if (t <= last) continue;
                         if (cnt == SM::T_CAP) {
                             over = true;
                             break;
                         }
-                        if (lane == 0) tlist[cnt] = t;
+                        const int64_t yt0 = (int64_t)J.qbase + (int64_t)J.qstride * t;
+                        const int64_t yt1 = (int64_t)J.qbase + (int64_t)J.qstride * min(t + BM - 1, J.n_q - 1);
+                        const bool wfull = yt0 >= run.x && yt1 < run.y &&
+                                           (int64_t)ly0 + (yt1 - y) - lkmin < args.mask.window;
+                        if (lane == 0) tlist[cnt] = wfull ? (int)((uint32_t)t | 0x80000000u) : t;
                         ++cnt;
                         last = t;
                     }
@@ -501,7 +511,9 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         }
     }
     const int steps = n_tiles * J.kv_group;   // (query head, tile) pairs, head-major
-    auto tile_q0 = [&](int t) { return use_list ? wave_uniform(tlist[t]) : i_begin + t * BM; };
+    // list entry or computed first query of tile t (bit 31: window-full, see above)
+    auto tile_entry = [&](int t) { return use_list ? wave_uniform(tlist[t]) : i_begin + t * BM; };
+    auto tile_q0 = [&](int t) { return tile_entry(t) & 0x7fffffff; };
 
     f32x16 acck[TT::DBLK], accv[TT::DBLK];
 #pragma unroll
@@ -557,7 +569,8 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         __builtin_amdgcn_s_waitcnt(0xF70);
         bwd_tile_barrier();
         if (step + 1 < steps) issue(slot ^ 1);
-        const int q0 = tile_q0(cur_tile);
+        const int entry = tile_entry(cur_tile);
+        const int q0 = entry & 0x7fffffff;
         if (++cur_tile == n_tiles) cur_tile = 0;
         const lds_byte* qt = lds + SM::Q_OFF + slot * TT::BYTES;
         const lds_byte* dt = lds + SM::DO_OFF + slot * TT::BYTES;
@@ -576,8 +589,9 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         const int yq1 = qbase + qstride * min(q0 + BM - 1, n_q - 1);
         bool full = yq0 >= kmax && (!tree || yq1 < hmin);
         if (WIN)   // and every pair within the window
-            full = full && (tree ? segp[yq0] == segp[yq1] && lposp[yq1] - lkmin < args.mask.window
-                                 : yq1 - pos_lo < args.mask.window);
+            full = full && (!tree ? yq1 - pos_lo < args.mask.window
+                            : use_list ? entry < 0
+                                       : segp[yq0] == segp[yq1] && lposp[yq1] - lkmin < args.mask.window);
         const auto* lqp = reinterpret_cast<const __attribute__((address_space(3))) int*>(lds + SM::LQ_OFF + slot * 256) + 8 * g;
         bf16x8 pb[2], dsb[2];
         // a row without gradient (LSE = -inf) gets p = 0
