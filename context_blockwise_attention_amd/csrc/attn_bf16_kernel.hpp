@@ -85,7 +85,8 @@ __device__ __forceinline__ u32x2 lds_tr4(const lds_byte* p) {
 // has a matrix phase and a softmax phase:
 //
 //   M(t): P(t-1) V(t-1) and S(t) = K(t) Q^T      -> 32 MFMAs per wave
-//   V(t): mask, row max, exp, row sum of S(t)     -> vector ALU only
+//   V(t): mask, exp, row sum of S(t) (row max     -> vector ALU only
+//         only when the reference must move)
 //
 // After the workgroup barrier that opens iteration t (t = tile sequence
 // index), group 0 (waves 0-3) runs M(t) then V(t) and group 1 runs V(t-1)
@@ -369,35 +370,58 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                     }
             }
         }
-        float mx = -INFINITY;
+        // Probabilities against the reference m (base 2, scaled), packed as
+        // the PV operands; returns this lane's sum of them.
+        auto probs = [&](float m) {
+            float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < TT::NKB; ++kb)
+            for (int kb = 0; kb < TT::NKB; ++kb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = xhalf_max(mx) * c2;
-        const bool raise = mx > m_run + kTau;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-            // rare: keeps the compiler from speculating the 64 accumulator
-            // multiplies (by 1) into every tile
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m));
+                    if (kb == 0 && i < 2) (i ? ps1 : ps0) = p;
+                    else if (i & 1) ps1 += p;
+                    else ps0 += p;
+                    pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
+                }
+            }
+            return ps0 + ps1;
+        };
+        // Fast path: once a row has a reference (m_run finite), its
+        // probabilities are taken against it directly, without the tile's
+        // max; they are kept only if every lane's sum stays within 2^kSumCap
+        // (no probability can then exceed it, and a NaN sum fails the test).
+        // Otherwise -- a row still without a reference, or scores that have
+        // risen far above it -- the tile is redone on the exact path: row
+        // max, reference raised lazily (by more than kTau), probabilities
+        // recomputed.  Either way acc, l_run and the probabilities share one
+        // reference, so the result is the same softmax.
+        float ps = 0.f;
+        bool exact = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+        if (!exact) {
+            ps = probs(m_run);
+            exact = __builtin_amdgcn_ballot_w64(!(ps <= kSumCap)) != 0;
+        }
+        if (exact) {
+            // rare: keeps the compiler from speculating the exact path's
+            // arithmetic (max, 64 accumulator multiplies) into every tile
             __builtin_amdgcn_sched_barrier(0);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < TT::NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+            mx = xhalf_max(mx) * c2;
+            const bool raise = mx > m_run + kTau;
             const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
             l_run *= alpha;
 #pragma unroll
             for (int b = 0; b < TT::DBLK; ++b) acc[b] *= alpha;
             m_run = raise ? mx : m_run;
+            ps = probs(m_run == -INFINITY ? 0.f : m_run);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < TT::NKB; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m_use));
-                if (i & 1) ps1 += p; else ps0 += p;
-                pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
-            }
-        }
-        l_run += ps0 + ps1;
+        l_run += ps;
     };
 
     // A workgroup barrier orders memory but not arithmetic: keep the compiler

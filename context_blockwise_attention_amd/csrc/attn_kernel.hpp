@@ -20,11 +20,13 @@
 //    the A operand of O^T += V^T P^T is one 16-byte LDS read per lane.
 //  * O^T accumulators: lane l holds its query's D/2 output values.
 //  * The running max is only raised when a tile's max exceeds it by more than
-//    2^kTau (in the base-2 exponent), so the accumulator rescale -- a pass
+//    kTau (in the base-2 exponent), so the accumulator rescale -- a pass
 //    over every accumulator register -- is rare; probabilities stay below
 //    2^kTau, far inside fp32 and bf16 range, and the final normalisation uses
 //    the same stale max for numerator and denominator, so the result is the
-//    same softmax.
+//    same softmax.  (The bf16 kernel goes one step further and skips the
+//    tile's max while the probabilities against the stale reference stay
+//    small: see softmax_phase in attn_bf16_kernel.hpp.)
 //  * Global loads go through buffer resources: 32-bit offsets, and rows past
 //    the end of a block read as zero (those keys are masked out).
 #pragma once
@@ -45,6 +47,7 @@ constexpr int kMaxJobs = 16;
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (base-2 exponent)
+constexpr float kSumCap = 65536.0f;   // bf16 kernel: largest per-lane tile sum kept without the tile max (2^16)
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit dwords (gfx9 family)
 
 enum MaskKind : int32_t { kCausal = 0, kTree = 1 };
