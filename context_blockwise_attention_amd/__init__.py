@@ -70,6 +70,7 @@ def lib():
         L.cpattn_version.restype = ctypes.c_int
         L.cpattn_mask_causal.argtypes = [ctypes.c_int64, ctypes.POINTER(P)]
         L.cpattn_mask_tree.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, P, ctypes.POINTER(P)]
+        L.cpattn_mask_tree_static.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, P, ctypes.POINTER(P)]
         L.cpattn_mask_free.argtypes = [P]
         L.cpattn_mask_with_window.argtypes = [P, ctypes.c_int64, P, ctypes.POINTER(P)]
         L.cpattn_mask_npos.argtypes = [P]
@@ -92,7 +93,8 @@ def lib():
         L.cpattn_ring_backward_chunks.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_float, P, P, P,
                                                   P, P, P, P]
         L.cpattn_sink_backward.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P, P, P]
-        for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_free", "cpattn_partial",
+        for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_tree_static", "cpattn_mask_free",
+                  "cpattn_partial",
                   "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan",
                   "cpattn_apply_sink", "cpattn_mask_with_window", "cpattn_backward_delta",
                   "cpattn_partial_backward", "cpattn_ring_backward", "cpattn_ring_backward_chunks",
@@ -170,6 +172,20 @@ class Mask:
         _check(lib().cpattn_mask_tree(seg.ctypes.data, seg.shape[0], par.ctypes.data, par.shape[0],
                                       _stream(stream), ctypes.byref(h)))
         return cls(h.value, int(seg.shape[0]), "tree")
+
+    @classmethod
+    def tree_static(cls, seg_id, parent, stream=None) -> "Mask":
+        """The same descriptor as :meth:`tree`, built without device
+        allocation into the library's static per-GPU buffer (at most 2^20
+        tokens and 2^16 segments).  Every call on a GPU returns the same
+        descriptor, replacing its previous contents."""
+        import numpy as np
+        seg = np.ascontiguousarray(seg_id, dtype=np.int32)
+        par = np.ascontiguousarray(parent, dtype=np.int32)
+        h = ctypes.c_void_p()
+        _check(lib().cpattn_mask_tree_static(seg.ctypes.data, seg.shape[0], par.ctypes.data, par.shape[0],
+                                             _stream(stream), ctypes.byref(h)))
+        return cls(h.value, int(seg.shape[0]), "tree-static")
 
     def with_window(self, window: int, stream=None) -> "Mask":
         """A new descriptor: this visibility restricted to keys within

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -64,6 +65,7 @@ struct cpattn_mask {
     int32_t* d_end = nullptr;     // [n_pos]
     int4* d_segtab = nullptr;     // [n_seg]
     int32_t* d_lpos = nullptr;    // [n_pos] logical positions (tree with a window)
+    bool is_static = false;       // device arrays in the library's static buffer (cpattn_mask_tree_static)
 };
 
 extern "C" int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out) {
@@ -78,7 +80,7 @@ extern "C" int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out) {
 }
 
 extern "C" int cpattn_mask_free(cpattn_mask* m) {
-    if (!m) return CPATTN_OK;
+    if (!m || m->is_static) return CPATTN_OK;   // a static descriptor belongs to the library
     hipError_t e1 = m->d_seg ? hipFree(m->d_seg) : hipSuccess;
     hipError_t e2 = m->d_end ? hipFree(m->d_end) : hipSuccess;
     hipError_t e3 = m->d_segtab ? hipFree(m->d_segtab) : hipSuccess;
@@ -93,50 +95,52 @@ extern "C" int cpattn_mask_free(cpattn_mask* m) {
 
 extern "C" int64_t cpattn_mask_npos(const cpattn_mask* m) { return m ? m->n_pos : -1; }
 
-// Builds the horizon representation of a prefix tree stored in depth-first
-// preorder: for each segment its run [run_start, run_end), its parent and the
-// end of its subtree; for each position its segment and subtree end.
-extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
-                                void* stream, cpattn_mask** out) {
-    if (!out) return fail(CPATTN_EINVAL, "cpattn_mask_tree: out is NULL");
-    *out = nullptr;
-    if (n_tok < 0 || n_tok > INT32_MAX) return fail(CPATTN_EINVAL, "cpattn_mask_tree: n_tok %lld out of range", (long long)n_tok);
-    if (n_seg < 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: n_seg < 0");
-    if ((n_tok > 0 && !seg_id) || (n_seg > 0 && !parent)) return fail(CPATTN_EINVAL, "cpattn_mask_tree: NULL array");
-    if (n_tok > 0 && n_seg == 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: tokens but no segments");
+// Validates a prefix tree stored in depth-first preorder and fills the host
+// parts of its descriptor: for each segment its run [run_start, run_end), its
+// parent and the end of its subtree (segs), the segments in storage order
+// (order) and the token count of each segment's strict ancestors (anc_len).
+// The vectors are only assigned within the capacity they already have when
+// it suffices (the no-allocation builder reserves it once).
+static int tree_host(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg, const char* who,
+                     std::vector<SegInfo>& segs, std::vector<int32_t>& order, std::vector<int32_t>& stack,
+                     std::vector<int64_t>& anc_len) {
+    if (n_tok < 0 || n_tok > INT32_MAX) return fail(CPATTN_EINVAL, "%s: n_tok %lld out of range", who, (long long)n_tok);
+    if (n_seg < 0) return fail(CPATTN_EINVAL, "%s: n_seg < 0", who);
+    if ((n_tok > 0 && !seg_id) || (n_seg > 0 && !parent)) return fail(CPATTN_EINVAL, "%s: NULL array", who);
+    if (n_tok > 0 && n_seg == 0) return fail(CPATTN_EINVAL, "%s: tokens but no segments", who);
 
-    std::vector<SegInfo> segs((size_t)n_seg, SegInfo{-1, -1, -1, -1});
+    segs.assign((size_t)n_seg, SegInfo{-1, -1, -1, -1});
     for (int32_t s = 0; s < n_seg; ++s) {
         if (parent[s] < -1 || parent[s] >= n_seg || parent[s] == s)
-            return fail(CPATTN_EINVAL, "cpattn_mask_tree: parent[%d] = %d out of range", s, parent[s]);
+            return fail(CPATTN_EINVAL, "%s: parent[%d] = %d out of range", who, s, parent[s]);
         segs[s].parent = parent[s];
     }
     // runs: every segment must be one contiguous, non-empty run
-    std::vector<int32_t> order;   // segments in storage order
+    order.clear();   // segments in storage order
     for (int64_t x = 0; x < n_tok; ++x) {
         int32_t s = seg_id[x];
-        if (s < 0 || s >= n_seg) return fail(CPATTN_EINVAL, "cpattn_mask_tree: seg_id[%lld] = %d out of range", (long long)x, s);
+        if (s < 0 || s >= n_seg) return fail(CPATTN_EINVAL, "%s: seg_id[%lld] = %d out of range", who, (long long)x, s);
         if (x == 0 || seg_id[x - 1] != s) {
             if (segs[s].run_start >= 0)
-                return fail(CPATTN_EINVAL, "cpattn_mask_tree: segment %d is split into several runs", s);
+                return fail(CPATTN_EINVAL, "%s: segment %d is split into several runs", who, s);
             segs[s].run_start = (int32_t)x;
             order.push_back(s);
         }
         segs[s].run_end = (int32_t)x + 1;
     }
     for (int32_t s = 0; s < n_seg; ++s)
-        if (segs[s].run_start < 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: segment %d has no token", s);
+        if (segs[s].run_start < 0) return fail(CPATTN_EINVAL, "%s: segment %d has no token", who, s);
     // cycles (a parent chain that never reaches a root)
     for (int32_t s = 0; s < n_seg; ++s) {
         int32_t cur = s;
         int32_t steps = 0;
         while (cur >= 0 && steps <= n_seg) { cur = segs[cur].parent; ++steps; }
-        if (cur >= 0) return fail(CPATTN_EINVAL, "cpattn_mask_tree: parent links of segment %d form a cycle", s);
+        if (cur >= 0) return fail(CPATTN_EINVAL, "%s: parent links of segment %d form a cycle", who, s);
     }
     // depth-first preorder: walking segments in storage order, the parent of
     // each must be on the stack of open ancestors; a segment's subtree closes
     // when a segment that is not its descendant starts.
-    std::vector<int32_t> stack;
+    stack.clear();
     for (size_t i = 0; i < order.size(); ++i) {
         int32_t s = order[i];
         int32_t p = segs[s].parent;
@@ -146,31 +150,72 @@ extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int3
         }
         if (p >= 0 && stack.empty())
             return fail(CPATTN_EUNSUPPORTED,
-                        "cpattn_mask_tree: segment %d is not stored inside its parent %d's subtree "
-                        "(the row must be in depth-first preorder)", s, p);
+                        "%s: segment %d is not stored inside its parent %d's subtree "
+                        "(the row must be in depth-first preorder)", who, s, p);
         stack.push_back(s);
     }
     while (!stack.empty()) {
         segs[stack.back()].subtree_end = (int32_t)n_tok;
         stack.pop_back();
     }
-
-    cpattn_mask* m = new (std::nothrow) cpattn_mask();
-    if (!m) return fail(CPATTN_ENOMEM, "cpattn_mask_tree: out of host memory");
-    m->kind = kTree;
-    m->n_pos = n_tok;
-    m->segs = segs;
-    m->run_order = order;
-    m->anc_len.assign((size_t)n_seg, 0);
+    anc_len.assign((size_t)n_seg, 0);
     for (int32_t sgi : order) {   // preorder: a parent's total is known before its children's
         const int32_t p = segs[sgi].parent;
-        m->anc_len[sgi] = p < 0 ? 0 : m->anc_len[p] + (segs[p].run_end - segs[p].run_start);
+        anc_len[sgi] = p < 0 ? 0 : anc_len[p] + (segs[p].run_end - segs[p].run_start);
     }
-    std::vector<int32_t> end((size_t)n_tok);
+    return CPATTN_OK;
+}
+
+// The device arrays of a tree descriptor, staged on the host: the subtree end
+// of each position and the segment table.
+static void tree_arrays(const int32_t* seg_id, int64_t n_tok, const std::vector<SegInfo>& segs,
+                        std::vector<int32_t>& end, std::vector<int4>& tab) {
+    end.resize((size_t)n_tok);
     for (int64_t x = 0; x < n_tok; ++x) end[x] = segs[seg_id[x]].subtree_end;
-    std::vector<int4> tab((size_t)n_seg);
-    for (int32_t s = 0; s < n_seg; ++s)
+    tab.resize(segs.size());
+    for (size_t s = 0; s < segs.size(); ++s)
         tab[s] = int4{segs[s].run_start, segs[s].run_end, segs[s].parent, segs[s].subtree_end};
+}
+
+// Uploads a tree descriptor's device arrays (enqueued on st, complete on return).
+static hipError_t tree_upload(int32_t* d_seg, int32_t* d_end, int4* d_segtab, const int32_t* seg_id, int64_t n_tok,
+                              const std::vector<int32_t>& end, const std::vector<int4>& tab, hipStream_t st) {
+    hipError_t e = hipSuccess;
+    if (n_tok > 0 &&
+        ((e = hipMemcpyAsync(d_seg, seg_id, sizeof(int32_t) * n_tok, hipMemcpyHostToDevice, st)) != hipSuccess ||
+         (e = hipMemcpyAsync(d_end, end.data(), sizeof(int32_t) * n_tok, hipMemcpyHostToDevice, st)) != hipSuccess))
+        return e;
+    if (!tab.empty() &&
+        (e = hipMemcpyAsync(d_segtab, tab.data(), sizeof(int4) * tab.size(), hipMemcpyHostToDevice, st)) != hipSuccess)
+        return e;
+    // the host staging arrays are released or reused after this call
+    return hipStreamSynchronize(st);
+}
+
+// Builds the horizon representation of a prefix tree stored in depth-first
+// preorder: for each segment its run [run_start, run_end), its parent and the
+// end of its subtree; for each position its segment and subtree end.
+extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
+                                void* stream, cpattn_mask** out) {
+    const char* who = "cpattn_mask_tree";
+    if (!out) return fail(CPATTN_EINVAL, "%s: out is NULL", who);
+    *out = nullptr;
+    std::vector<SegInfo> segs;
+    std::vector<int32_t> order, stack;
+    std::vector<int64_t> anc_len;
+    int rc = tree_host(seg_id, n_tok, parent, n_seg, who, segs, order, stack, anc_len);
+    if (rc != CPATTN_OK) return rc;
+
+    cpattn_mask* m = new (std::nothrow) cpattn_mask();
+    if (!m) return fail(CPATTN_ENOMEM, "%s: out of host memory", who);
+    m->kind = kTree;
+    m->n_pos = n_tok;
+    m->segs = std::move(segs);
+    m->run_order = std::move(order);
+    m->anc_len = std::move(anc_len);
+    std::vector<int32_t> end;
+    std::vector<int4> tab;
+    tree_arrays(seg_id, n_tok, m->segs, end, tab);
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     size_t nb = sizeof(int32_t) * (size_t)std::max<int64_t>(n_tok, 1);
@@ -179,26 +224,99 @@ extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int3
     if ((e = hipMalloc(&m->d_seg, nb)) != hipSuccess || (e = hipMalloc(&m->d_end, nb)) != hipSuccess ||
         (e = hipMalloc(&m->d_segtab, tb)) != hipSuccess) {
         cpattn_mask_free(m);
-        return fail(CPATTN_ENOMEM, "cpattn_mask_tree: hipMalloc: %s", hipGetErrorString(e));
+        return fail(CPATTN_ENOMEM, "%s: hipMalloc: %s", who, hipGetErrorString(e));
     }
-    if (n_tok > 0) {
-        if ((e = hipMemcpyAsync(m->d_seg, seg_id, sizeof(int32_t) * n_tok, hipMemcpyHostToDevice, st)) != hipSuccess ||
-            (e = hipMemcpyAsync(m->d_end, end.data(), sizeof(int32_t) * n_tok, hipMemcpyHostToDevice, st)) != hipSuccess) {
-            cpattn_mask_free(m);
-            return hip_fail(e, "cpattn_mask_tree: upload");
-        }
-    }
-    if (n_seg > 0 &&
-        (e = hipMemcpyAsync(m->d_segtab, tab.data(), sizeof(int4) * n_seg, hipMemcpyHostToDevice, st)) != hipSuccess) {
-        cpattn_mask_free(m);
-        return hip_fail(e, "cpattn_mask_tree: upload");
-    }
-    // the host staging vectors die with this call
-    if ((e = hipStreamSynchronize(st)) != hipSuccess) {
+    if ((e = tree_upload(m->d_seg, m->d_end, m->d_segtab, seg_id, n_tok, end, tab, st)) != hipSuccess) {
         cpattn_mask_free(m);
         return hip_fail(e, "cpattn_mask_tree: upload");
     }
     *out = m;
+    return CPATTN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// tree descriptor without device allocation (cpattn_mask_tree_static)
+// ---------------------------------------------------------------------------
+// The device arrays live in `scratch`, a static buffer of the library: one
+// copy per GPU, which keeps the last call's descriptor until the process
+// ends.  Host code never uses the array's name as an address (in host code it
+// is only a handle): the device address is taken once per device with
+// hipGetSymbolAddress and kept in the device's slot.
+constexpr int64_t kStaticMaxTok = CPATTN_STATIC_MAX_TOK;
+constexpr int32_t kStaticMaxSeg = CPATTN_STATIC_MAX_SEG;
+constexpr size_t kStaticEndOff = sizeof(int32_t) * (size_t)kStaticMaxTok;       // seg at 0, end after it
+constexpr size_t kStaticTabOff = 2 * sizeof(int32_t) * (size_t)kStaticMaxTok;   // segment table (int4)
+constexpr size_t kStaticBytes = kStaticTabOff + sizeof(int4) * (size_t)kStaticMaxSeg;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+struct StaticMaskSlot {
+    bool ready = false;
+    unsigned char* dev = nullptr;   // this device's copy of `scratch`
+    cpattn_mask mask;               // host side of the descriptor, reused call after call
+    std::vector<int32_t> stack, end;
+    std::vector<int4> tab;
+};
+static StaticMaskSlot g_static_slots[kMaxDevices];
+static std::mutex g_static_init;
+
+// Device address of `scratch` and host capacity for the largest tree, once
+// per device (the only allocations of this path, on its first call).
+static int static_slot(StaticMaskSlot** out, const char* who) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "cpattn_mask_tree_static: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CPATTN_EUNSUPPORTED, "%s: device %d out of range", who, dev);
+    StaticMaskSlot& sl = g_static_slots[dev];
+    std::lock_guard<std::mutex> lock(g_static_init);
+    if (!sl.ready) {
+        void* ptr = nullptr;
+        if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+            return hip_fail(e, "cpattn_mask_tree_static: hipGetSymbolAddress");
+        sl.dev = static_cast<unsigned char*>(ptr);
+        sl.mask.segs.reserve(kStaticMaxSeg);
+        sl.mask.run_order.reserve(kStaticMaxSeg);
+        sl.mask.anc_len.reserve(kStaticMaxSeg);
+        sl.stack.reserve(kStaticMaxSeg);
+        sl.end.reserve((size_t)kStaticMaxTok);
+        sl.tab.reserve(kStaticMaxSeg);
+        sl.ready = true;
+    }
+    *out = &sl;
+    return CPATTN_OK;
+}
+
+extern "C" int cpattn_mask_tree_static(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
+                                       void* stream, cpattn_mask** out) {
+    const char* who = "cpattn_mask_tree_static";
+    if (!out) return fail(CPATTN_EINVAL, "%s: out is NULL", who);
+    *out = nullptr;
+    if (n_tok > kStaticMaxTok || n_seg > kStaticMaxSeg)
+        return fail(CPATTN_EUNSUPPORTED, "%s: %lld tokens / %d segments exceed the static descriptor's capacity "
+                    "(%lld tokens, %d segments); use cpattn_mask_tree", who, (long long)n_tok, n_seg,
+                    (long long)kStaticMaxTok, kStaticMaxSeg);
+    StaticMaskSlot* sl = nullptr;
+    int rc = static_slot(&sl, who);
+    if (rc != CPATTN_OK) return rc;
+    cpattn_mask& m = sl->mask;
+    // the previous descriptor of this device is replaced (also on failure)
+    m.kind = kTree;
+    m.n_pos = 0;
+    m.is_static = true;
+    m.window = 0;
+    m.d_lpos = nullptr;
+    rc = tree_host(seg_id, n_tok, parent, n_seg, who, m.segs, m.run_order, sl->stack, m.anc_len);
+    if (rc != CPATTN_OK) return rc;
+    tree_arrays(seg_id, n_tok, m.segs, sl->end, sl->tab);
+    m.d_seg = reinterpret_cast<int32_t*>(sl->dev);
+    m.d_end = reinterpret_cast<int32_t*>(sl->dev + kStaticEndOff);
+    m.d_segtab = reinterpret_cast<int4*>(sl->dev + kStaticTabOff);
+    hipError_t e = tree_upload(m.d_seg, m.d_end, m.d_segtab, seg_id, n_tok, sl->end, sl->tab,
+                               reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cpattn_mask_tree_static: upload");
+    m.n_pos = n_tok;
+    *out = &m;
     return CPATTN_OK;
 }
 

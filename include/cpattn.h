@@ -18,7 +18,8 @@
  *  - Memory: tensors, outputs and position data passed to compute calls are
  *    device pointers owned by the caller, who keeps them alive until the
  *    stream has finished with them.  The library allocates device memory only
- *    inside mask descriptors (released by cpattn_mask_free).
+ *    inside mask descriptors (released by cpattn_mask_free), and holds one
+ *    static buffer per GPU for cpattn_mask_tree_static.
  *  - Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
  *    Compute calls validate their arguments synchronously, then enqueue work
  *    on the stream and return without waiting.  A launch failure returns
@@ -43,7 +44,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 7
+#define CPATTN_VERSION_MINOR 8
 
 typedef enum {
     CPATTN_OK = 0,
@@ -106,6 +107,27 @@ int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out);
  * complete when the function returns (the host arrays may be freed). */
 int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
                      void* stream, cpattn_mask** out);
+
+/* cpattn_mask_tree for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops that build a descriptor per input,
+ * harnesses that forbid hipMalloc): the same descriptor, same arguments,
+ * checks and errors, built without any device allocation.  Its device arrays
+ * live in a static buffer of the library, one per GPU, held until the process
+ * ends: at most CPATTN_STATIC_MAX_TOK tokens and CPATTN_STATIC_MAX_SEG
+ * segments (9 MiB), larger trees return EUNSUPPORTED.  The descriptor returned
+ * belongs to the library and is the same object on every call on the current
+ * device: each call replaces that device's previous descriptor (its device
+ * arrays are rewritten in order on `stream`; work still using the previous
+ * one must be on `stream` or finished), and calls that overlap on one GPU
+ * (other threads or streams) race.  cpattn_mask_free accepts it and does
+ * nothing.  It is used like any descriptor, cpattn_mask_with_window included
+ * (whose result is an ordinary, allocated descriptor).  The first call on a
+ * device looks up the buffer's device address and reserves host bookkeeping
+ * for the largest tree; later calls allocate nothing. */
+#define CPATTN_STATIC_MAX_TOK (1 << 20)
+#define CPATTN_STATIC_MAX_SEG (1 << 16)
+int cpattn_mask_tree_static(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg,
+                            void* stream, cpattn_mask** out);
 
 /* Sliding-window attention on logical positions ("Context Parallelism in
  * ART", section 06): a new descriptor with the visibility of `m` restricted

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_error_string(L):
     import context_blockwise_attention_amd as cp
-    assert cp.version() == (0, 7)
+    assert cp.version() == (0, 8)
     assert isinstance(L.cpattn_last_error(), bytes)
 
 
@@ -74,6 +74,21 @@ def test_tree_descriptor_rejections(L, seg, parent, code):
     rc = L.cpattn_mask_tree(s.ctypes.data, len(s), p.ctypes.data, len(p), None, ctypes.byref(h))
     assert rc == code, L.cpattn_last_error()
     assert L.cpattn_last_error().startswith(b"cpattn_mask_tree")
+
+
+def test_static_tree_descriptor_limits(L):
+    """The no-allocation tree descriptor rejects trees beyond its static
+    buffer (2^20 tokens, 2^16 segments) before any device work."""
+    h = ctypes.c_void_p()
+    n = (1 << 20) + 1
+    seg = np.zeros(n, dtype=np.int32)
+    par = np.full(1, -1, dtype=np.int32)
+    assert L.cpattn_mask_tree_static(seg.ctypes.data, n, par.ctypes.data, 1, None, ctypes.byref(h)) == EUNSUPPORTED
+    assert b"capacity" in L.cpattn_last_error()
+    par = np.full((1 << 16) + 1, -1, dtype=np.int32)
+    assert L.cpattn_mask_tree_static(seg.ctypes.data, 10, par.ctypes.data, len(par), None,
+                                     ctypes.byref(h)) == EUNSUPPORTED
+    assert L.cpattn_mask_tree_static(seg.ctypes.data, 10, par.ctypes.data, 1, None, None) == EINVAL
 
 
 def _partial(L, cp, q, k, v, mask, qpos=(0, 1), kpos=(0, 1), scale=0.1, o=0x2000, lse=0x3000, acc=0):
