@@ -96,20 +96,21 @@ __device__ __forceinline__ u32x2 lds_tr4(const lds_byte* p) {
 // phases (forcing the alternation) made the second matrix phase of every
 // iteration markedly slower and cost ~15% per tile.
 //
-// Group 0 issues every load, in its softmax phase: V(t+1) as the phase
-// opens, K(t+2) and E(t+2) once its tile walk has produced tile t+2; each
-// wave loads a quarter of a tile.  Group 0's half of an iteration is the
-// shorter one (it reaches the next barrier well before group 1), while group
-// 1's softmax phase leads into the second matrix phase of the iteration and
-// lies on the critical path, so it carries neither loads nor their address
-// and LDS-destination arithmetic.  Before the barrier that opens iteration
-// t+1 the loading waves wait for their own older loads, leaving in flight
-// only the ones issued in iteration t: a tile gets about an iteration and a
-// half to arrive before a matrix phase reads it, which hides the HBM/L2
-// latency (all workgroups of a head walk the same tiles at about the same
-// time, so most of them wait on the same miss).  K and V rotate over 3
-// buffers, E over 4: every buffer a load overwrites was last read before the
-// barrier that precedes the load.  (Wider key tiles would halve the
+// Loads are split between the groups: group 0 issues V(t+1) as its softmax
+// phase opens, group 1 issues K(t+2) and E(t+2) after its matrix phase, in
+// the time it would otherwise wait at the barrier; each wave loads a quarter
+// of a tile.  (A load instruction holds its wave until the CU's load path
+// accepts it, about 1 KB per 16 cycles for the whole CU, so the issuing
+// wave pays for the tile's transfer; measured per iteration, group 0's
+// softmax phase is its longest stretch and group 1 finishes its matrix phase
+// early.)  Before the barrier that opens iteration t+1 every wave waits for
+// its own older loads, leaving in flight only the ones issued in iteration
+// t: V gets about an iteration and a half and K about one iteration to
+// arrive before a matrix phase reads it, which hides the HBM/L2 latency (all
+// workgroups of a head walk the same tiles at about the same time, so most
+// of them wait on the same miss).  K and V rotate over 3 buffers, E over 4:
+// every buffer a load overwrites was last read before the barrier that
+// precedes the load.  (Wider key tiles would halve the
 // barriers per key, but 128-key scores and probabilities do not fit the 256
 // registers a wave has at two waves per SIMD.)
 // ---------------------------------------------------------------------------
@@ -258,13 +259,14 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     // Wait until at most `pending` of this wave's vector-memory loads are in
     // flight (vmcnt only; the immediate leaves expcnt and lgkmcnt unwaited):
     // the largest immediate not above `pending` among the counts that occur
-    // (one tile of V, K and E, or V alone).  Loads complete in issue order, so
-    // this waits for every older load.
+    // (a quarter tile of V, or of K with or without E; the prologue's K, E and
+    // V).  Loads complete in issue order, so this waits for every older load.
     auto wait_older = [&](int pending) {
         constexpr int NI = TT::NI;
         static_assert(2 * NI + 1 < 16, "vmcnt immediate");
         if (pending >= 2 * NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI + 1));
         else if (pending >= 2 * NI) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NI));
+        else if (pending >= NI + 1) __builtin_amdgcn_s_waitcnt(0xF70 | (NI + 1));
         else if (pending >= NI) __builtin_amdgcn_s_waitcnt(0xF70 | NI);
         else __builtin_amdgcn_s_waitcnt(0xF70);
     };
@@ -481,12 +483,12 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         if (!cur.next(kblk, args.mask, y1, &t_cur, &f_cur)) break;   // tile 0
         bool h_nxt = cur.next(kblk, args.mask, y1, &t_nxt, &f_nxt);
         bool h_n2 = false;
-        // horizon loads per tile of this wave (group 0 loads them)
-        const int e_loads = (G == 0 && tree && wl < (WIN ? 2 : 1) * (BN / 64)) ? 1 : 0;
+        // horizon loads per tile of this wave (group 0 in the prologue, group 1 after)
+        const int e_loads = (tree && wl < (WIN ? 2 : 1) * (BN / 64)) ? 1 : 0;
         // this wave's loads issued in the current iteration (they may stay in
         // flight across the next barrier)
         int pending = 0;
-        // K/E of tile t+2 (group 0, after its tile walk has produced it)
+        // K/E of tile s of the walk into buffer slot s
         auto issue_ke = [&](int tile, int s) {
             issue_kv(k_rsrc, voffk, k_st, tile, kbuf(s));
             if (tree) issue_e(tile, s);
@@ -507,13 +509,14 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(1));
             softmax_phase(t_cur, f_cur, ebuf(0));
             h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
-            if (h_n2) issue_ke(t_n2, 2);
-            pending = (h_nxt ? TT::NI : 0) + (h_n2 ? TT::NI + e_loads : 0);   // V(1), K(2), E(2)
+            pending = h_nxt ? TT::NI : 0;   // V(1)
         } else {
             h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
             phase_barrier();                                            // barrier 1
             qk(kbuf(0));
             m_schedule(false, true);
+            if (h_n2) issue_ke(t_n2, 2);   // K(2), E(2)
+            pending = h_n2 ? TT::NI + e_loads : 0;
         }
         int t = 1;
         while (h_nxt) {
@@ -535,8 +538,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                 if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(t + 1));
                 softmax_phase(t_cur, f_cur, ebuf(t));
                 h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
-                if (h_n2) issue_ke(t_n2, t + 2);
-                pending = (h_nxt ? TT::NI : 0) + (h_n2 ? TT::NI + e_loads : 0);
+                pending = h_nxt ? TT::NI : 0;
             } else {
                 h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
                 softmax_phase(t_prev, f_prev, ebuf(t - 1));
@@ -545,6 +547,9 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                 qk(kbuf(t));
                 m_schedule(true, true);
                 matrix_priority(false);
+                // K(t+2), E(t+2): issued while this group would wait at the barrier
+                if (h_n2) issue_ke(t_n2, t + 2);
+                pending = h_n2 ? TT::NI + e_loads : 0;
             }
             ++t;
         }
