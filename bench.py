@@ -331,6 +331,139 @@ def backward_ring(cp, torch, dev, qd, kd, vd, seg, parent, N, outs, A, steps: in
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def _gpu_qkv(torch, dev, seed, H, n, d, n_q=None):
+    """Seeded N(0, 1) Q, K, V drawn on the GPU and rounded to bf16 (timing
+    legs only: the parity of these workloads is tested against the oracle in
+    tests/, with the CPU-drawn inputs of workloads.qkv)."""
+    g = torch.Generator(device=dev).manual_seed(int(seed))
+    mk = lambda rows: torch.randn((H, rows, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    return mk(n if n_q is None else n_q), mk(n), mk(n)
+
+
+def _timed(torch, stream, fn, reps: int, warmup: int = 2):
+    """(mean ms from HIP events on the stream, wall ms per call) over reps calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    return e0.elapsed_time(e1) / reps, wall
+
+
+def _rate(flops, ms):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def config_legs(cp, workloads, torch, dev, reps: int = 10, seeds: int = 16):
+    """The other bf16 workloads at full size, each timed as the ring call a
+    rank (or every rank) makes, visible-pair TFLOP/s (pairs from
+    cpattn_ring_plan, exact):
+    * causal ring: 32 heads x 32768 tokens, 8 contiguous blocks of 4096, all
+      ranks (one call);
+    * striped: P = 4 over 65536 positions, rank 0's 16384 queries against the
+      four stripes (rounds visit stripes 0, 3, 2, 1);
+    * 131072-token rows of seeded families, one GPU's share of a 4-way split:
+      each rank's 32768 queries against the 4 blocks of 32768, per seed
+      0..seeds-1 with the tree (and its descriptor) rebuilt per seed, and the
+      same Q/K/V ("Context Parallelism in ART", section 12: measured trees
+      distinct from the warmup trees; a CP step lasts as long as its slowest
+      rank)."""
+    H, d = 32, 128
+    stream = torch.cuda.current_stream()
+    out = {}
+    # causal ring, all 8 ranks
+    n, N = 32768, 8
+    c = n // N
+    q, k, v = _gpu_qkv(torch, dev, 0, H, n, d)
+    mask = cp.Mask.causal(n)
+    pos = [(r * c, 1) for r in range(N)]
+    pairs = int(cp.ring_plan([c] * N, pos, mask).sum())
+    assert pairs == n * (n + 1) // 2
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    Q, K, V = blk(q), blk(k), blk(v)
+    outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
+                torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
+    ms, wall = _timed(torch, stream, lambda: cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream), reps)
+    flops = 4.0 * d * H * pairs
+    out["causal_ring"] = dict({"workload": "causal, 32 heads x 32768 tokens, d 128, bf16, ring of 8 blocks of 4096, "
+                                           "all ranks", "visible_pairs_per_head": pairs, "ms_per_step": round(ms, 4),
+                               "wall_ms_per_step": round(wall, 4)}, **_rate(flops, ms))
+    mask.free()
+    del q, k, v, Q, K, V, outs
+    # striped, rank 0
+    n, P = 65536, 4
+    nq = n // P
+    q, k, v = _gpu_qkv(torch, dev, 0, H, n, d, n_q=nq)   # q = rank 0's queries (positions 4 i)
+    idx = [torch.arange(r, n, P, device=dev) for r in range(P)]
+    K = [k.index_select(1, i).contiguous() for i in idx]
+    V = [v.index_select(1, i).contiguous() for i in idx]
+    del k, v
+    Q = [q] + [None] * (P - 1)
+    mask = cp.Mask.causal(n)
+    pos = [(r, P) for r in range(P)]
+    pairs = int(cp.ring_plan([nq] * P, pos, mask)[0].sum())
+    assert pairs == nq * (nq + 1) // 2 + (P - 1) * nq * (nq - 1) // 2
+    o0 = {0: (torch.empty((H, nq, d), dtype=torch.float32, device=dev),
+              torch.empty((H, nq), dtype=torch.float32, device=dev))}
+    ms, wall = _timed(torch, stream, lambda: cp.ring_emulate(Q, K, V, pos, mask, ranks=[0], outs=o0, stream=stream),
+                      reps)
+    flops = 4.0 * d * H * pairs
+    out["striped"] = dict({"workload": "striped P = 4 over 65536 positions (x % 4 == r), rank 0's 16384 queries, "
+                                       "4 rounds, 32 heads, d 128, bf16", "visible_pairs_per_head": pairs,
+                           "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall, 4)}, **_rate(flops, ms))
+    mask.free()
+    del q, K, V, Q, o0
+    # 131072-token rows of seeded families, ranks 0-3 of a 4-way split
+    n, N = 131072, 4
+    c = n // N
+    q, k, v = _gpu_qkv(torch, dev, 0, H, n, d)
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    Q, K, V = blk(q), blk(k), blk(v)
+    pos = [(r * c, 1) for r in range(N)]
+    outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
+                torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
+    series = []
+    tot_pairs = tot_ms = 0.0
+    for seed in range(seeds):
+        seg, parent = workloads.tree_families(seed, n)
+        t0 = time.perf_counter()
+        mask = cp.Mask.tree(seg, parent)
+        desc_ms = (time.perf_counter() - t0) * 1e3
+        work = cp.ring_plan([c] * N, pos, mask)   # [rank, round] visible pairs
+        rank_ms, rank_wall = [], []
+        for r in range(N):
+            ms, wall = _timed(torch, stream,
+                              lambda: cp.ring_emulate(Q, K, V, pos, mask, ranks=[r], outs={r: outs[r]}, stream=stream),
+                              3, warmup=1)
+            rank_ms.append(ms)
+            rank_wall.append(wall)
+        mask.free()
+        pairs_r = [int(x) for x in work.sum(axis=1)]
+        tot_pairs += sum(pairs_r)
+        tot_ms += sum(rank_ms)
+        series.append({"seed": seed, "segments": int(len(parent)), "per_rank_ms": [round(x, 4) for x in rank_ms],
+                       "per_rank_wall_ms": [round(x, 4) for x in rank_wall], "per_rank_pairs": pairs_r,
+                       "slowest_rank_ms": round(max(rank_ms), 4), "descriptor_ms": round(desc_ms, 3),
+                       "TFLOP/s": round(4.0 * d * H * sum(pairs_r) / (sum(rank_ms) * 1e-3) / 1e12, 2)})
+    flops_all = 4.0 * d * H * tot_pairs
+    out["tree128k_share"] = dict({
+        "workload": "131072 tokens of seeded families (prompt 2048-16384, 2-8 completions of 1024-8192, tree mask "
+                    "per family), 32 heads, d 128, bf16; each of the 4 ranks' 32768 queries against the 4 blocks of "
+                    "32768, timed per rank; seeds 0-%d, descriptor rebuilt per seed" % (seeds - 1),
+        "seeds": seeds, "ms_all_ranks_all_seeds": round(tot_ms, 3),
+        "slowest_rank_ms_mean": round(float(np.mean([s_["slowest_rank_ms"] for s_ in series])), 4),
+        "per_seed": series}, **_rate(flops_all, tot_ms))
+    del q, k, v, Q, K, V, outs
+    return out
+
+
 def ring_sizes(cp, torch, dev, qd, kd, vd, mask, seg, parent, flops, sizes=(1, 8), steps: int = 10):
     """The same row as rings of other sizes (one block of 65536; eight of
     8192): forward ring step time and visible-pair TFLOP/s."""
@@ -365,6 +498,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing (diagnostic runs)")
     ap.add_argument("--no-balance", action="store_true",
                     help="skip the extra legs (ring sizes, zig-zag comparison, GQA, window, backward)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (causal ring, striped, 131072-token families)")
+    ap.add_argument("--only-configs", action="store_true",
+                    help="profiling run: only the other workloads' legs (no headline, prints their JSON)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="calibration run: only time a plain device copy of this many MiB")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -397,6 +534,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib}))
+        return
+    if args.only_configs:
+        print(json.dumps({"configs": config_legs(cp, workloads, torch, dev)}), flush=True)
         return
     H, d = 32, 128
     P, C = 24576, (8192,) * 5
@@ -523,6 +663,8 @@ def main():
                   "frac_of_hbm_peak": round(merge_gbs / PEAK_HBM_GBS, 4)},
     }
 
+    if not args.no_configs:
+        result["configs"] = config_legs(cp, workloads, torch, dev)
     if not args.no_balance:
         result["load_balance"] = load_balance(cp, workloads, torch, dev)
         result["ring_sizes"] = ring_sizes(cp, torch, dev, qd, kd, vd, mask, seg, parent, flops)
@@ -554,7 +696,7 @@ def main():
         cpu_s = time.perf_counter() - t0
         cpu_tflops = 4.0 * d * pairs / cpu_s / 1e12
         result["cpu_baseline"] = {
-            "value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": "%d query rows per head x %d heads of the same row (%d visible pairs), fp64 C/OpenMP, "
                       "%.2f s" % (rows_per_head, H, pairs, cpu_s),
             "extrapolated_full_step_s": round(flops / (cpu_tflops * 1e12), 1),
@@ -603,6 +745,17 @@ def main():
                                 "frac_of_hbm_peak": round(mb_bytes / (mb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     mask.free()
     print(json.dumps(result), flush=True)
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def _time_reps(torch, stream, reps, fn):

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/cpattn.h"
@@ -54,6 +55,29 @@ struct SegInfo {
     int32_t run_start, run_end, parent, subtree_end;
 };
 
+// Host-side pair counts of a (query block, key block) layout, cached in the
+// descriptor (it is immutable), so that repeated ring calls over the same
+// layout do no per-row host work.
+struct PairKey {
+    int64_t v[6];   // q base, q stride, q rows, k base, k stride, k rows
+    bool operator==(const PairKey& o) const { return std::memcmp(v, o.v, sizeof v) == 0; }
+};
+struct PairKeyHash {
+    size_t operator()(const PairKey& k) const {
+        uint64_t h = 1469598103934665603ull;   // FNV-1a over the six fields
+        for (int i = 0; i < 6; ++i) {
+            h ^= (uint64_t)k.v[i];
+            h *= 1099511628211ull;
+        }
+        return (size_t)h;
+    }
+};
+struct PairStats {
+    int64_t exact = -1;       // visible pairs (-1: not computed yet)
+    double estimate = -1.0;   // sampled estimate used to order a launch's jobs
+};
+constexpr size_t kPairCacheMax = 4096;
+
 struct cpattn_mask {
     int32_t kind;                 // kCausal or kTree
     int64_t n_pos;
@@ -66,6 +90,8 @@ struct cpattn_mask {
     int4* d_segtab = nullptr;     // [n_seg]
     int32_t* d_lpos = nullptr;    // [n_pos] logical positions (tree with a window)
     bool is_static = false;       // device arrays in the library's static buffer (cpattn_mask_tree_static)
+    mutable std::mutex pair_mu;   // guards pair_cache (calls may come from several threads)
+    mutable std::unordered_map<PairKey, PairStats, PairKeyHash> pair_cache;
 };
 
 extern "C" int cpattn_mask_causal(int64_t n_pos, cpattn_mask** out) {
@@ -301,6 +327,10 @@ extern "C" int cpattn_mask_tree_static(const int32_t* seg_id, int64_t n_tok, con
     if (rc != CPATTN_OK) return rc;
     cpattn_mask& m = sl->mask;
     // the previous descriptor of this device is replaced (also on failure)
+    {
+        std::lock_guard<std::mutex> lock(m.pair_mu);
+        m.pair_cache.clear();   // no allocation: the map keeps its buckets
+    }
     m.kind = kTree;
     m.n_pos = 0;
     m.is_static = true;
@@ -408,9 +438,24 @@ static int check_posmap(cpattn_posmap p, int64_t n, const cpattn_mask* m, const 
 static int64_t pair_count(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk,
                           int64_t step);
 
+// pair_count over every row, and the sampled estimate, remembered per layout
+static int64_t pair_exact(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
+    const PairKey key{{qp.base, qp.stride, nq, kp.base, kp.stride, nk}};
+    {
+        std::lock_guard<std::mutex> lock(m->pair_mu);
+        auto it = m->pair_cache.find(key);
+        if (it != m->pair_cache.end() && it->second.exact >= 0) return it->second.exact;
+    }
+    const int64_t c = pair_count(m, qp, nq, kp, nk, 1);
+    std::lock_guard<std::mutex> lock(m->pair_mu);
+    if (m->pair_cache.size() >= kPairCacheMax) m->pair_cache.clear();
+    m->pair_cache[key].exact = c;
+    return c;
+}
+
 static bool pair_nonempty(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
     if (nq == 0 || nk == 0) return false;
-    if (m->window > 0) return pair_count(m, qp, nq, kp, nk, 1) > 0;   // exact, per query row
+    if (m->window > 0) return pair_exact(m, qp, nq, kp, nk) > 0;   // exact, per query row
     const int64_t qmax = qp.base + qp.stride * (nq - 1);
     auto first_query_at_or_after = [&](int64_t x) -> int64_t {
         if (x <= qp.base) return qp.base;
@@ -478,7 +523,17 @@ static int64_t pair_count(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cp
 // Approximate visible pairs from about 256 evenly spaced query rows; orders
 // the jobs of a launch.
 static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
-    return (double)pair_count(m, qp, nq, kp, nk, std::max<int64_t>(1, nq / 256));
+    const PairKey key{{qp.base, qp.stride, nq, kp.base, kp.stride, nk}};
+    {
+        std::lock_guard<std::mutex> lock(m->pair_mu);
+        auto it = m->pair_cache.find(key);
+        if (it != m->pair_cache.end() && it->second.estimate >= 0.0) return it->second.estimate;
+    }
+    const double e = (double)pair_count(m, qp, nq, kp, nk, std::max<int64_t>(1, nq / 256));
+    std::lock_guard<std::mutex> lock(m->pair_mu);
+    if (m->pair_cache.size() >= kPairCacheMax) m->pair_cache.clear();
+    m->pair_cache[key].estimate = e;
+    return e;
 }
 
 // ---------------------------------------------------------------------------
@@ -805,7 +860,7 @@ extern "C" int cpattn_ring_plan(int N, int C, const int64_t* n_tok, const cpattn
             int64_t w = 0;
             for (int c = 0; c < C; ++c)
                 for (int c2 = 0; c2 < C; ++c2)
-                    w += pair_count(mask, pos[r * C + c], n_tok[r * C + c], pos[b * C + c2], n_tok[b * C + c2], 1);
+                    w += pair_exact(mask, pos[r * C + c], n_tok[r * C + c], pos[b * C + c2], n_tok[b * C + c2]);
             work[r * N + kk] = w;
         }
     return CPATTN_OK;

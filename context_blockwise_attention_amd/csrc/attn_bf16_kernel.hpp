@@ -398,16 +398,19 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         // max, reference raised lazily (by more than kTau), probabilities
         // recomputed.  Either way acc, l_run and the probabilities share one
         // reference, so the result is the same softmax.
+        // (The windowed instantiation always takes the exact path: keeping
+        // the scores live through the fast path's check next to the window's
+        // registers spilled.)
         float ps = 0.f;
-        bool exact = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+        bool exact = WIN || __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
         if (!exact) {
             ps = probs(m_run);
             exact = __builtin_amdgcn_ballot_w64(!(ps <= kSumCap)) != 0;
         }
         if (exact) {
-            // rare: keeps the compiler from speculating the exact path's
-            // arithmetic (max, 64 accumulator multiplies) into every tile
-            __builtin_amdgcn_sched_barrier(0);
+            // (rare without a window) keeps the compiler from speculating the
+            // exact path's arithmetic into every tile
+            if (!WIN) __builtin_amdgcn_sched_barrier(0);
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < TT::NKB; ++kb)
@@ -415,13 +418,18 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
             mx = xhalf_max(mx) * c2;
             const bool raise = mx > m_run + kTau;
-            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-            l_run *= alpha;
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                // rare: keeps the compiler from speculating the 64 accumulator
+                // multiplies (by 1) into every tile
+                __builtin_amdgcn_sched_barrier(0);
+                const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+                l_run *= alpha;
 #pragma unroll
-            for (int b = 0; b < TT::DBLK; ++b) acc[b] *= alpha;
-            m_run = raise ? mx : m_run;
+                for (int b = 0; b < TT::DBLK; ++b) acc[b] *= alpha;
+                m_run = raise ? mx : m_run;
+            }
             ps = probs(m_run == -INFINITY ? 0.f : m_run);
-            __builtin_amdgcn_sched_barrier(0);
+            if (!WIN) __builtin_amdgcn_sched_barrier(0);
         }
         l_run += ps;
     };
@@ -483,7 +491,13 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         if (!cur.next(kblk, args.mask, y1, &t_cur, &f_cur)) break;   // tile 0
         bool h_nxt = cur.next(kblk, args.mask, y1, &t_nxt, &f_nxt);
         bool h_n2 = false;
-        // horizon loads per tile of this wave (group 0 in the prologue, group 1 after)
+        // Loads of K and E after the prologue: by group 1 (see the load
+        // schedule above), except with a window, where group 0 issues every
+        // load (measured: the window's partial tiles lengthen group 1's
+        // softmax phase, and the split made the windowed ring ~1.5% slower)
+        constexpr bool kSplitLoads = !WIN;
+        // horizon loads per tile of this wave (group 0 in the prologue, then
+        // the group that loads K)
         const int e_loads = (tree && wl < (WIN ? 2 : 1) * (BN / 64)) ? 1 : 0;
         // this wave's loads issued in the current iteration (they may stay in
         // flight across the next barrier)
@@ -509,14 +523,15 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(1));
             softmax_phase(t_cur, f_cur, ebuf(0));
             h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
-            pending = h_nxt ? TT::NI : 0;   // V(1)
+            if (!kSplitLoads && h_n2) issue_ke(t_n2, 2);
+            pending = (h_nxt ? TT::NI : 0) + (!kSplitLoads && h_n2 ? TT::NI + e_loads : 0);   // V(1) (K(2), E(2))
         } else {
             h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
             phase_barrier();                                            // barrier 1
             qk(kbuf(0));
             m_schedule(false, true);
-            if (h_n2) issue_ke(t_n2, 2);   // K(2), E(2)
-            pending = h_n2 ? TT::NI + e_loads : 0;
+            if (kSplitLoads && h_n2) issue_ke(t_n2, 2);   // K(2), E(2)
+            pending = kSplitLoads && h_n2 ? TT::NI + e_loads : 0;
         }
         int t = 1;
         while (h_nxt) {
@@ -538,7 +553,8 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                 if (h_nxt) issue_kv(v_rsrc, voffv, v_st, t_nxt, vbuf(t + 1));
                 softmax_phase(t_cur, f_cur, ebuf(t));
                 h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
-                pending = h_nxt ? TT::NI : 0;
+                if (!kSplitLoads && h_n2) issue_ke(t_n2, t + 2);
+                pending = (h_nxt ? TT::NI : 0) + (!kSplitLoads && h_n2 ? TT::NI + e_loads : 0);
             } else {
                 h_n2 = h_nxt && cur.next(kblk, args.mask, y1, &t_n2, &f_n2);
                 softmax_phase(t_prev, f_prev, ebuf(t - 1));
@@ -548,8 +564,8 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
                 m_schedule(true, true);
                 matrix_priority(false);
                 // K(t+2), E(t+2): issued while this group would wait at the barrier
-                if (h_n2) issue_ke(t_n2, t + 2);
-                pending = h_n2 ? TT::NI + e_loads : 0;
+                if (kSplitLoads && h_n2) issue_ke(t_n2, t + 2);
+                pending = kSplitLoads && h_n2 ? TT::NI + e_loads : 0;
             }
             ++t;
         }

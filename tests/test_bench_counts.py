@@ -1,9 +1,9 @@
 """Host-side counts that bench.py reports (visible pairs per row, per
 (query block, key block) pair, and the tiles the partial kernel executes),
 checked by brute force on small random packed trees: a dense boolean
-visibility matrix built from the tree's definition ("Prefix Tree Packing",
-visibility of a packed token: its own segment up to itself, and every token
-of every strict ancestor segment)."""
+visibility matrix built from the tree's definition ("Context Parallelism in
+ART", sections 01-02: a packed token sees its own segment up to itself and
+every token of every strict ancestor segment)."""
 import numpy as np
 import pytest
 
