@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "../../include/cpattn.h"
+#include "host_tree.hpp"
 #include "attn_bf16_kernel.hpp"
 #include "attn_bwd_bf16_kernel.hpp"
 #include "attn_bwd_kernel.hpp"
@@ -51,9 +52,9 @@ extern "C" int cpattn_version(void) { return (CPATTN_VERSION_MAJOR << 16) | CPAT
 // ---------------------------------------------------------------------------
 // visibility descriptor
 // ---------------------------------------------------------------------------
-struct SegInfo {
-    int32_t run_start, run_end, parent, subtree_end;
-};
+using cpattn_host::HostTree;
+using cpattn_host::SegInfo;
+static_assert(cpattn_host::kKindCausal == kCausal && cpattn_host::kKindTree == kTree, "mask kinds");
 
 // Host-side pair counts of a (query block, key block) layout, cached in the
 // descriptor (it is immutable), so that repeated ring calls over the same
@@ -78,13 +79,8 @@ struct PairStats {
 };
 constexpr size_t kPairCacheMax = 4096;
 
-struct cpattn_mask {
-    int32_t kind;                 // kCausal or kTree
-    int64_t n_pos;
-    std::vector<SegInfo> segs;    // host copy (tree)
-    std::vector<int32_t> run_order;   // segments by run start (tree)
-    std::vector<int64_t> anc_len;     // tokens of the strict ancestors of each segment (tree)
-    int32_t window = 0;           // sliding window in logical positions (0 = none)
+// host part (kind, positions, segment runs, window) plus the device arrays
+struct cpattn_mask : HostTree {
     int32_t* d_seg = nullptr;     // [n_pos]
     int32_t* d_end = nullptr;     // [n_pos]
     int4* d_segtab = nullptr;     // [n_seg]
@@ -120,77 +116,6 @@ extern "C" int cpattn_mask_free(cpattn_mask* m) {
 }
 
 extern "C" int64_t cpattn_mask_npos(const cpattn_mask* m) { return m ? m->n_pos : -1; }
-
-// Validates a prefix tree stored in depth-first preorder and fills the host
-// parts of its descriptor: for each segment its run [run_start, run_end), its
-// parent and the end of its subtree (segs), the segments in storage order
-// (order) and the token count of each segment's strict ancestors (anc_len).
-// The vectors are only assigned within the capacity they already have when
-// it suffices (the no-allocation builder reserves it once).
-static int tree_host(const int32_t* seg_id, int64_t n_tok, const int32_t* parent, int32_t n_seg, const char* who,
-                     std::vector<SegInfo>& segs, std::vector<int32_t>& order, std::vector<int32_t>& stack,
-                     std::vector<int64_t>& anc_len) {
-    if (n_tok < 0 || n_tok > INT32_MAX) return fail(CPATTN_EINVAL, "%s: n_tok %lld out of range", who, (long long)n_tok);
-    if (n_seg < 0) return fail(CPATTN_EINVAL, "%s: n_seg < 0", who);
-    if ((n_tok > 0 && !seg_id) || (n_seg > 0 && !parent)) return fail(CPATTN_EINVAL, "%s: NULL array", who);
-    if (n_tok > 0 && n_seg == 0) return fail(CPATTN_EINVAL, "%s: tokens but no segments", who);
-
-    segs.assign((size_t)n_seg, SegInfo{-1, -1, -1, -1});
-    for (int32_t s = 0; s < n_seg; ++s) {
-        if (parent[s] < -1 || parent[s] >= n_seg || parent[s] == s)
-            return fail(CPATTN_EINVAL, "%s: parent[%d] = %d out of range", who, s, parent[s]);
-        segs[s].parent = parent[s];
-    }
-    // runs: every segment must be one contiguous, non-empty run
-    order.clear();   // segments in storage order
-    for (int64_t x = 0; x < n_tok; ++x) {
-        int32_t s = seg_id[x];
-        if (s < 0 || s >= n_seg) return fail(CPATTN_EINVAL, "%s: seg_id[%lld] = %d out of range", who, (long long)x, s);
-        if (x == 0 || seg_id[x - 1] != s) {
-            if (segs[s].run_start >= 0)
-                return fail(CPATTN_EINVAL, "%s: segment %d is split into several runs", who, s);
-            segs[s].run_start = (int32_t)x;
-            order.push_back(s);
-        }
-        segs[s].run_end = (int32_t)x + 1;
-    }
-    for (int32_t s = 0; s < n_seg; ++s)
-        if (segs[s].run_start < 0) return fail(CPATTN_EINVAL, "%s: segment %d has no token", who, s);
-    // cycles (a parent chain that never reaches a root)
-    for (int32_t s = 0; s < n_seg; ++s) {
-        int32_t cur = s;
-        int32_t steps = 0;
-        while (cur >= 0 && steps <= n_seg) { cur = segs[cur].parent; ++steps; }
-        if (cur >= 0) return fail(CPATTN_EINVAL, "%s: parent links of segment %d form a cycle", who, s);
-    }
-    // depth-first preorder: walking segments in storage order, the parent of
-    // each must be on the stack of open ancestors; a segment's subtree closes
-    // when a segment that is not its descendant starts.
-    stack.clear();
-    for (size_t i = 0; i < order.size(); ++i) {
-        int32_t s = order[i];
-        int32_t p = segs[s].parent;
-        while (!stack.empty() && stack.back() != p) {
-            segs[stack.back()].subtree_end = segs[s].run_start;
-            stack.pop_back();
-        }
-        if (p >= 0 && stack.empty())
-            return fail(CPATTN_EUNSUPPORTED,
-                        "%s: segment %d is not stored inside its parent %d's subtree "
-                        "(the row must be in depth-first preorder)", who, s, p);
-        stack.push_back(s);
-    }
-    while (!stack.empty()) {
-        segs[stack.back()].subtree_end = (int32_t)n_tok;
-        stack.pop_back();
-    }
-    anc_len.assign((size_t)n_seg, 0);
-    for (int32_t sgi : order) {   // preorder: a parent's total is known before its children's
-        const int32_t p = segs[sgi].parent;
-        anc_len[sgi] = p < 0 ? 0 : anc_len[p] + (segs[p].run_end - segs[p].run_start);
-    }
-    return CPATTN_OK;
-}
 
 // The device arrays of a tree descriptor, staged on the host: the subtree end
 // of each position and the segment table.
@@ -229,7 +154,7 @@ extern "C" int cpattn_mask_tree(const int32_t* seg_id, int64_t n_tok, const int3
     std::vector<SegInfo> segs;
     std::vector<int32_t> order, stack;
     std::vector<int64_t> anc_len;
-    int rc = tree_host(seg_id, n_tok, parent, n_seg, who, segs, order, stack, anc_len);
+    int rc = cpattn_host::tree_host(seg_id, n_tok, parent, n_seg, who, fail, segs, order, stack, anc_len);
     if (rc != CPATTN_OK) return rc;
 
     cpattn_mask* m = new (std::nothrow) cpattn_mask();
@@ -336,7 +261,7 @@ extern "C" int cpattn_mask_tree_static(const int32_t* seg_id, int64_t n_tok, con
     m.is_static = true;
     m.window = 0;
     m.d_lpos = nullptr;
-    rc = tree_host(seg_id, n_tok, parent, n_seg, who, m.segs, m.run_order, sl->stack, m.anc_len);
+    rc = cpattn_host::tree_host(seg_id, n_tok, parent, n_seg, who, fail, m.segs, m.run_order, sl->stack, m.anc_len);
     if (rc != CPATTN_OK) return rc;
     tree_arrays(seg_id, n_tok, m.segs, sl->end, sl->tab);
     m.d_seg = reinterpret_cast<int32_t*>(sl->dev);
@@ -372,10 +297,8 @@ extern "C" int cpattn_mask_with_window(const cpattn_mask* m, int64_t window, voi
         hipStream_t st = reinterpret_cast<hipStream_t>(stream);
         const size_t nb = sizeof(int32_t) * (size_t)std::max<int64_t>(m->n_pos, 1);
         const size_t tb = sizeof(int4) * std::max<size_t>(m->segs.size(), 1);
-        std::vector<int32_t> lpos((size_t)m->n_pos);
-        for (int32_t sg : m->run_order)
-            for (int32_t x = m->segs[sg].run_start; x < m->segs[sg].run_end; ++x)
-                lpos[x] = (int32_t)(m->anc_len[sg] + x - m->segs[sg].run_start);
+        std::vector<int32_t> lpos;
+        cpattn_host::tree_lpos(*m, lpos);
         hipError_t e;
         if ((e = hipMalloc(&w->d_seg, nb)) != hipSuccess || (e = hipMalloc(&w->d_end, nb)) != hipSuccess ||
             (e = hipMalloc(&w->d_segtab, tb)) != hipSuccess || (e = hipMalloc(&w->d_lpos, nb)) != hipSuccess) {
@@ -433,10 +356,6 @@ static int check_posmap(cpattn_posmap p, int64_t n, const cpattn_mask* m, const 
     return CPATTN_OK;
 }
 
-// Does any query of the block see any key of the block?  Exact for both masks
-// (per segment, the smallest key position gives the widest chance).
-static int64_t pair_count(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk,
-                          int64_t step);
 
 // pair_count over every row, and the sampled estimate, remembered per layout
 static int64_t pair_exact(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
@@ -446,78 +365,18 @@ static int64_t pair_exact(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cp
         auto it = m->pair_cache.find(key);
         if (it != m->pair_cache.end() && it->second.exact >= 0) return it->second.exact;
     }
-    const int64_t c = pair_count(m, qp, nq, kp, nk, 1);
+    const int64_t c = cpattn_host::pair_count(*m, qp, nq, kp, nk, 1);
     std::lock_guard<std::mutex> lock(m->pair_mu);
     if (m->pair_cache.size() >= kPairCacheMax) m->pair_cache.clear();
     m->pair_cache[key].exact = c;
     return c;
 }
 
+// Does any query of the block see any key of the block?  Exact for both masks.
 static bool pair_nonempty(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk) {
     if (nq == 0 || nk == 0) return false;
     if (m->window > 0) return pair_exact(m, qp, nq, kp, nk) > 0;   // exact, per query row
-    const int64_t qmax = qp.base + qp.stride * (nq - 1);
-    auto first_query_at_or_after = [&](int64_t x) -> int64_t {
-        if (x <= qp.base) return qp.base;
-        int64_t i = (x - qp.base + qp.stride - 1) / qp.stride;
-        return qp.base + qp.stride * i;
-    };
-    if (m->kind == kCausal) return kp.base <= qmax;
-    const int64_t kmax = kp.base + kp.stride * (nk - 1);
-    for (const SegInfo& s : m->segs) {
-        int64_t lo = std::max<int64_t>(s.run_start, kp.base);
-        int64_t hi = std::min<int64_t>(s.run_end - 1, kmax);
-        if (lo > hi) continue;
-        int64_t j = (lo - kp.base + kp.stride - 1) / kp.stride;   // first key of the block in the run
-        int64_t xa = kp.base + kp.stride * j;
-        if (xa > hi) continue;
-        int64_t y = first_query_at_or_after(xa);
-        if (y <= qmax && y < s.subtree_end) return true;
-    }
-    return false;
-}
-
-// Number of keys of a block (positions base + stride * j, j < n) inside the
-// position range [a, b].
-static int64_t keys_in_range(cpattn_posmap kp, int64_t nk, int64_t a, int64_t b) {
-    if (a > b || nk == 0) return 0;
-    auto ceil_div = [](int64_t x, int64_t y) { return x >= 0 ? (x + y - 1) / y : -((-x) / y); };
-    auto floor_div = [](int64_t x, int64_t y) { return x >= 0 ? x / y : -((-x + y - 1) / y); };
-    const int64_t lo = std::max<int64_t>(0, ceil_div(a - kp.base, kp.stride));
-    const int64_t hi = std::min<int64_t>(nk - 1, floor_div(b - kp.base, kp.stride));
-    return hi >= lo ? hi - lo + 1 : 0;
-}
-
-// Visible (query, key) pairs of a block pair, counted on every step-th query
-// row and scaled by step (exact for step = 1).
-static int64_t pair_count(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, cpattn_posmap kp, int64_t nk,
-                          int64_t step) {
-    if (nq == 0 || nk == 0) return 0;
-    int64_t sum = 0;
-    for (int64_t i = 0; i < nq; i += step) {
-        const int64_t y = qp.base + qp.stride * i;
-        // keys of a run of segment s (positions [a, b]) whose logical position
-        // (x - run_start + anc_len) is within the window of the query's
-        const int64_t W = m->window;
-        if (m->kind == kCausal) {
-            sum += keys_in_range(kp, nk, W > 0 ? std::max<int64_t>(0, y - W + 1) : 0, y);
-            continue;
-        }
-        // segment of position y: the last run starting at or before y
-        auto it = std::upper_bound(m->run_order.begin(), m->run_order.end(), y,
-                                   [&](int64_t v, int32_t seg) { return v < m->segs[seg].run_start; });
-        int32_t sg = *(it - 1);
-        const int64_t ly = m->anc_len[sg] + y - m->segs[sg].run_start;
-        auto clip = [&](int32_t s2) {   // first position of s2's run inside the window
-            const int64_t lbase = m->segs[s2].run_start - m->anc_len[s2];
-            return W > 0 ? std::max<int64_t>(m->segs[s2].run_start, ly - W + 1 + lbase) : (int64_t)m->segs[s2].run_start;
-        };
-        int64_t c = keys_in_range(kp, nk, clip(sg), y);
-        for (int32_t a = m->segs[sg].parent; a >= 0; a = m->segs[a].parent)
-            c += keys_in_range(kp, nk, clip(a), m->segs[a].run_end - 1);
-        sum += c;
-    }
-    return sum * step;
+    return cpattn_host::pair_nonempty_nowin(*m, qp, nq, kp, nk);
 }
 
 // Approximate visible pairs from about 256 evenly spaced query rows; orders
@@ -529,7 +388,7 @@ static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, 
         auto it = m->pair_cache.find(key);
         if (it != m->pair_cache.end() && it->second.estimate >= 0.0) return it->second.estimate;
     }
-    const double e = (double)pair_count(m, qp, nq, kp, nk, std::max<int64_t>(1, nq / 256));
+    const double e = (double)cpattn_host::pair_count(*m, qp, nq, kp, nk, std::max<int64_t>(1, nq / 256));
     std::lock_guard<std::mutex> lock(m->pair_mu);
     if (m->pair_cache.size() >= kPairCacheMax) m->pair_cache.clear();
     m->pair_cache[key].estimate = e;
