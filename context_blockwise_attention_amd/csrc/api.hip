@@ -743,20 +743,29 @@ extern "C" int cpattn_merge(int n_parts, const float* const* o_parts, const floa
     }
     bool all_aligned = vec;
     for (int p = 0; p < n_parts; ++p) all_aligned = all_aligned && (reinterpret_cast<uintptr_t>(o_parts[p]) & 15) == 0;
-    a.vec = all_aligned ? 4 : 1;
+    const int unit = all_aligned ? 4 : 1;
     a.o_out = o_out;
     a.l_out = lse_out;
     a.rows = n_rows;
     a.n = n_parts;
     a.d = (int32_t)d;
-    const int64_t units = a.vec == 4 ? d / 4 : d;
+    const int64_t units = d / unit;
     a.tpr = (int32_t)std::min<int64_t>(256, std::max<int64_t>(1, units));
     // round threads-per-row down to a divisor of 256 so rows never straddle workgroups
     while (256 % a.tpr) --a.tpr;
     const int64_t rows_per_block = 256 / a.tpr;
     const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many rows", who);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    using MergeFn = void (*)(MergeArgs);
+    static const MergeFn vec4[9] = {merge_kernel<0, 4>, merge_kernel<1, 4>, merge_kernel<2, 4>,
+                                    merge_kernel<3, 4>, merge_kernel<4, 4>, merge_kernel<5, 4>,
+                                    merge_kernel<6, 4>, merge_kernel<7, 4>, merge_kernel<8, 4>};
+    static const MergeFn vec1[9] = {merge_kernel<0, 1>, merge_kernel<1, 1>, merge_kernel<2, 1>,
+                                    merge_kernel<3, 1>, merge_kernel<4, 1>, merge_kernel<5, 1>,
+                                    merge_kernel<6, 1>, merge_kernel<7, 1>, merge_kernel<8, 1>};
+    const int np = n_parts <= 8 ? n_parts : 0;
+    hipLaunchKernelGGL(unit == 4 ? vec4[np] : vec1[np], dim3((unsigned)blocks), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? CPATTN_OK : hip_fail(e, "merge launch");
 }

@@ -23,60 +23,110 @@ struct MergeArgs {
     int32_t n;
     int32_t d;
     int32_t tpr;   // threads per row (consecutive threads of one workgroup)
-    int32_t vec;   // 4 when d % 4 == 0, else 1
 };
 
+// One row's d floats move as VEC-float units (VEC = 4 when d % 4 == 0 and
+// every row start is 16-byte aligned, else 1).
+template <int VEC> struct MergeUnit;
+template <> struct MergeUnit<4> { using T = float4; };
+template <> struct MergeUnit<1> { using T = float; };
+
+__device__ __forceinline__ void merge_axpy(float4& acc, float w, const float4& v) {
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+}
+__device__ __forceinline__ void merge_axpy(float& acc, float w, float v) { acc += w * v; }
+
+// NP = n when 1 <= n <= 8: every LSE and every part's unit of a chunk is
+// loaded before any arithmetic, so a thread has all n loads in flight, and the
+// weights w_p are computed once per row.  NP = 0 serves any n in groups of 8
+// (the last group's surplus slots re-read the final part with weight 0).
+template <int NP, int VEC>
 __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
+    using U = typename MergeUnit<VEC>::T;
+    constexpr int G = NP > 0 ? NP : 8;
     const int rows_per_block = 256 / a.tpr;
     const int sub = threadIdx.x / a.tpr;
     const int t = threadIdx.x % a.tpr;
     const int64_t row = (int64_t)blockIdx.x * rows_per_block + sub;
     const bool active = sub < rows_per_block && row < a.rows;
+    const int n = NP > 0 ? NP : a.n;
 
     float m = -INFINITY;
     float z = 0.f;
+    float w[G];
     if (active) {
-        for (int p = 0; p < a.n; ++p) m = fmaxf(m, a.l[p][row]);
-        if (m != -INFINITY)
-            for (int p = 0; p < a.n; ++p) z += expf(a.l[p][row] - m);
+        if (NP > 0) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) w[j] = a.l[j][row];
+#pragma unroll
+            for (int j = 0; j < G; ++j) m = fmaxf(m, w[j]);
+            const float ms = m == -INFINITY ? 0.f : m;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                w[j] = expf(w[j] - ms);
+                z += w[j];
+            }
+        } else {
+            for (int p0 = 0; p0 < n; p0 += G) {
+#pragma unroll
+                for (int j = 0; j < G; ++j) w[j] = a.l[min(p0 + j, n - 1)][row];
+#pragma unroll
+                for (int j = 0; j < G; ++j) m = fmaxf(m, w[j]);
+            }
+            if (m != -INFINITY)
+                for (int p0 = 0; p0 < n; p0 += G) {
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {
+                        const float e = expf(a.l[min(p0 + j, n - 1)][row] - m);
+                        z += p0 + j < n ? e : 0.f;
+                    }
+                }
+        }
     }
-    // every thread has read its LSEs before any output LSE is written (the
-    // output may alias part 0)
-    __syncthreads();
-    if (!active) return;
     const bool empty = m == -INFINITY;
     const float rz = empty ? 0.f : 1.f / z;
-    if (a.vec == 4) {
-        const int chunks = a.d / 4;
-        for (int c = t; c < chunks; c += a.tpr) {
-            float4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (!empty) {
-                for (int p = 0; p < a.n; ++p) {
-                    const float w = expf(a.l[p][row] - m);
-                    const float4 v = reinterpret_cast<const float4*>(a.o[p] + row * a.d)[c];
-                    acc.x += w * v.x;
-                    acc.y += w * v.y;
-                    acc.z += w * v.z;
-                    acc.w += w * v.w;
+    // every thread has read its LSEs before any output LSE is written (the
+    // output may alias part 0, and a row may span several waves)
+    __syncthreads();
+    if (active && !empty) {
+        const int units = a.d / VEC;
+        for (int c = t; c < units; c += a.tpr) {
+            U acc{};
+            if (NP > 0) {
+                U v[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) v[j] = reinterpret_cast<const U*>(a.o[j] + row * a.d)[c];
+                // the scheduler would otherwise wait for each load before issuing the next
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < G; ++j) merge_axpy(acc, w[j] * rz, v[j]);
+            } else {
+                for (int p0 = 0; p0 < n; p0 += G) {
+                    U v[G];
+                    float lp[G];
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {
+                        const int p = min(p0 + j, n - 1);
+                        lp[j] = a.l[p][row];
+                        v[j] = reinterpret_cast<const U*>(a.o[p] + row * a.d)[c];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < G; ++j) merge_axpy(acc, p0 + j < n ? expf(lp[j] - m) * rz : 0.f, v[j]);
                 }
-                acc.x *= rz;
-                acc.y *= rz;
-                acc.z *= rz;
-                acc.w *= rz;
             }
-            reinterpret_cast<float4*>(a.o_out + row * a.d)[c] = acc;
+            reinterpret_cast<U*>(a.o_out + row * a.d)[c] = acc;
         }
-    } else {
-        for (int c = t; c < a.d; c += a.tpr) {
-            float acc = 0.f;
-            if (!empty) {
-                for (int p = 0; p < a.n; ++p) acc += expf(a.l[p][row] - m) * a.o[p][row * a.d + c];
-                acc *= rz;
-            }
-            a.o_out[row * a.d + c] = acc;
-        }
+    } else if (active) {
+        for (int c = t; c < a.d / VEC; c += a.tpr) reinterpret_cast<U*>(a.o_out + row * a.d)[c] = U{};
     }
-    if (t == 0) a.l_out[row] = empty ? -INFINITY : m + logf(z);
+    // the general form re-reads the LSEs above: all of the block's threads are
+    // past that before the output LSE (possibly part 0's) is written
+    if (NP == 0) __syncthreads();
+    if (active && t == 0) a.l_out[row] = empty ? -INFINITY : m + logf(z);
 }
 
 // (O, LSE) = (0, -inf) for rows that saw no key at all.

@@ -163,20 +163,39 @@ def test_ring_tree_all_ranks(cp, N):
         _cmp(out[r][0], out[r][1], O[:, lay[r]], L[:, lay[r]], "bf16", "rank %d" % r)
 
 
-def test_merge_kernel(cp):
-    rng = np.random.default_rng(0)
+def _merge_parts(n_parts, rows, d, seed):
+    rng = np.random.default_rng(seed)
     parts = []
-    for p in range(5):
-        O = rng.standard_normal((3, 77, 128))
-        L = rng.standard_normal((3, 77)) * 4
-        L[p % 3, p * 5:(p * 5 + 7)] = -np.inf
-        O[p % 3, p * 5:(p * 5 + 7)] = 0
+    for p in range(n_parts):
+        O = rng.standard_normal((3, rows, d))
+        L = rng.standard_normal((3, rows)) * 4
+        L[p % 3, p * 5 % rows:(p * 5 % rows + 7)] = -np.inf   # rows this part never saw
+        O[p % 3, p * 5 % rows:(p * 5 % rows + 7)] = 0
+        L[:, 0] = -np.inf                                       # a row empty in every part
+        O[:, 0] = 0
         parts.append((O.astype(np.float32), L.astype(np.float32)))
-    parts[0][1][:, 0] = -np.inf   # a row empty in every part
-    for p in parts:
-        p[1][:, 0] = -np.inf
-        p[0][:, 0] = 0
+    return parts
+
+
+def test_merge_kernel(cp):
+    parts = _merge_parts(5, 77, 128, 0)
     Om, Lm = oracle.merge([(a.astype(np.float64), b.astype(np.float64)) for a, b in parts])
     dev = [(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()) for a, b in parts]
     o, l = cp.merge(dev)
     _cmp(o, l, Om, Lm, "f32", "merge")
+
+
+# every part count the kernel unrolls (1..8), the grouped form (9, 17, 64
+# parts), rows of 1-float units (d % 4 != 0), short rows, and rows that span
+# several waves (d = 1024: 256 threads per row)
+@pytest.mark.parametrize("n_parts,d", [(1, 128), (2, 128), (3, 64), (4, 128), (6, 100), (7, 36), (8, 128),
+                                       (9, 128), (17, 20), (64, 8), (4, 1024), (12, 1024), (3, 2), (2, 1)])
+def test_merge_kernel_shapes(cp, n_parts, d):
+    parts = _merge_parts(n_parts, 45, d, 100 + n_parts)
+    Om, Lm = oracle.merge([(a.astype(np.float64), b.astype(np.float64)) for a, b in parts])
+    dev = [(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()) for a, b in parts]
+    o, l = cp.merge(dev)
+    _cmp(o, l, Om, Lm, "f32", "merge of %d parts, d %d" % (n_parts, d))
+    # the output may alias part 0 (documented in-place use)
+    cp.merge(dev, out=dev[0])
+    _cmp(dev[0][0], dev[0][1], Om, Lm, "f32", "in-place merge of %d parts, d %d" % (n_parts, d))
