@@ -599,11 +599,11 @@ def main():
     # standalone merge (materialised partials): rank N-1's 4 partials -> one
     merge_parts = [(torch.randn((H, c, d), device=dev), torch.randn((H, c), device=dev)) for _ in range(N)]
     mo = (torch.empty((H, c, d), device=dev), torch.empty((H, c), device=dev))
-    for _ in range(3):
+    reps = 20
+    for _ in range(reps):
         cp.merge(merge_parts, out=mo)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 20
     e0.record(stream)
     for _ in range(reps):
         cp.merge(merge_parts, out=mo)
@@ -709,7 +709,7 @@ def main():
     so = torch.cat([outs[r][0] for r in range(N)], 1).contiguous()
     sl = torch.cat([outs[r][1] for r in range(N)], 1).contiguous()
     sink = torch.zeros((H,), dtype=torch.float32, device=dev)
-    for _ in range(3):
+    for _ in range(reps):
         cp.apply_sink(so, sl, sink)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -743,6 +743,26 @@ def main():
                                 "ms": round(mb_ms, 4), "bytes": mb_bytes,
                                 "GB/s": round(mb_bytes / (mb_ms * 1e-3) / 1e9, 1),
                                 "frac_of_hbm_peak": round(mb_bytes / (mb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    # the bandwidth the HBM-bound legs are measured against: a plain streaming
+    # read and copy of 2 GiB by the library's probe kernel, best over a few
+    # grid sizes (the data-sheet HBM figure is not reached by a plain stream)
+    pb = 2 ** 31
+    p_src = torch.zeros(pb // 4, dtype=torch.float32, device=dev)
+    p_dst = torch.empty(pb // 4, dtype=torch.float32, device=dev)
+    ceil = {}
+    for kind, moved in (("read", pb), ("copy", 2 * pb)):
+        best = None
+        for grid in (1024, 2048, 8192, 0):
+            ms_k = _time_reps(torch, stream, 5, lambda: cp.stream_probe(kind, p_src, p_dst, grid=grid, stream=stream))
+            gbs = moved / (ms_k * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, grid)
+        ceil[kind] = {"GB/s": round(best[0], 1), "grid": best[1] or "one lane per 16 B",
+                      "frac_of_hbm_peak": round(best[0] / PEAK_HBM_GBS, 4)}
+    del p_src, p_dst
+    result["hbm_ceiling"] = {"kernel": "stream_probe_kernel", "bytes": pb, **ceil}
+    for leg in ("merge", "sink", "sink_backward", "merge_backward"):
+        result[leg]["frac_of_measured_copy"] = round(result[leg]["GB/s"] / ceil["copy"]["GB/s"], 4)
     mask.free()
     print(json.dumps(result), flush=True)
 
@@ -759,7 +779,9 @@ def _cpu_model() -> str:
 
 
 def _time_reps(torch, stream, reps, fn):
-    for _ in range(3):
+    # short HBM-bound launches read several percent slow on their first few
+    # repetitions after a buffer is first touched: warm up longer than the reps
+    for _ in range(max(10, reps)):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

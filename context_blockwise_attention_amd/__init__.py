@@ -93,13 +93,14 @@ def lib():
         L.cpattn_ring_backward_chunks.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_float, P, P, P,
                                                   P, P, P, P]
         L.cpattn_sink_backward.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P, P, P]
+        L.cpattn_stream_probe.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int, P]
         for f in ("cpattn_mask_causal", "cpattn_mask_tree", "cpattn_mask_tree_static", "cpattn_mask_free",
                   "cpattn_partial",
                   "cpattn_merge", "cpattn_ring_emulate", "cpattn_ring_emulate_chunks", "cpattn_ring_plan",
                   "cpattn_apply_sink", "cpattn_mask_with_window", "cpattn_backward_delta",
                   "cpattn_partial_backward", "cpattn_ring_backward", "cpattn_ring_backward_chunks",
                   "cpattn_merge_backward",
-                  "cpattn_sink_backward"):
+                  "cpattn_sink_backward", "cpattn_stream_probe"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -536,3 +537,20 @@ def ring_backward(q_blocks, k_blocks, v_blocks, pos, mask: Mask, lses, deltas, d
                                       float(_default_scale(d) if scale is None else scale), lp, dp, od, gq, gk, gv,
                                       _stream(stream)))
     return grads
+
+
+def stream_probe(kind: str, src: torch.Tensor, dst: torch.Tensor, grid: int = 0, stream=None):
+    """Measurement helper (not part of the attention path): one streaming
+    ``"read"`` of ``src`` or ``"copy"`` of ``src`` into ``dst`` by the
+    library's plain grid-stride kernel, ``grid`` workgroups (0: one lane per
+    16 bytes)."""
+    if kind not in ("read", "copy"):
+        raise ValueError("kind must be 'read' or 'copy'")
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous device tensors")
+    nbytes = src.numel() * src.element_size()
+    need = nbytes if kind == "copy" else 16
+    if dst.numel() * dst.element_size() < need:
+        raise ValueError("dst is too small")
+    _check(lib().cpattn_stream_probe(0 if kind == "read" else 1, src.data_ptr(), dst.data_ptr(), nbytes, int(grid),
+                                     _stream(stream)))

@@ -24,6 +24,7 @@
 #include "attn_bwd_kernel.hpp"
 #include "attn_kernel.hpp"
 #include "merge_kernel.hpp"
+#include "probe_kernel.hpp"
 
 using namespace cpattn;
 
@@ -1013,6 +1014,30 @@ static int check_bwd_common(const cpattn_tensor* q, const cpattn_tensor* dout, c
         return fail(CPATTN_EINVAL, "%s: dout must match q in dtype, heads, tokens and head dim", who);
     if (q->n_tok > 0 && (!lse || !delta)) return fail(CPATTN_EINVAL, "%s: lse or delta is NULL", who);
     return CPATTN_OK;
+}
+
+extern "C" int cpattn_stream_probe(int kind, const void* src, void* dst, int64_t bytes, int grid, void* stream) {
+    const char* who = "cpattn_stream_probe";
+    if (kind != 0 && kind != 1) return fail(CPATTN_EINVAL, "%s: kind must be 0 (read) or 1 (copy)", who);
+    if (bytes < 0 || bytes % 16 != 0) return fail(CPATTN_EINVAL, "%s: bytes must be a non-negative multiple of 16", who);
+    if (grid > (1 << 20)) return fail(CPATTN_EINVAL, "%s: grid above 2^20 workgroups", who);
+    if (bytes == 0) return CPATTN_OK;
+    if (!src || !dst) return fail(CPATTN_EINVAL, "%s: NULL pointer", who);
+    if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) != 0)
+        return fail(CPATTN_EUNSUPPORTED, "%s: src and dst must be 16-byte aligned", who);
+    const int64_t units = bytes / 16;
+    const int64_t full = (units + 255) / 256;
+    const int64_t blocks = grid > 0 ? std::min<int64_t>(grid, full) : full;
+    if (blocks > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many bytes", who);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    float4* d4 = reinterpret_cast<float4*>(dst);
+    if (kind == 0)
+        hipLaunchKernelGGL(stream_probe_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, s4, d4, units);
+    else
+        hipLaunchKernelGGL(stream_probe_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, s4, d4, units);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CPATTN_OK : hip_fail(e, "stream probe launch");
 }
 
 extern "C" int cpattn_backward_delta(const float* o, const cpattn_tensor* dout, float* delta, void* stream) {

@@ -44,7 +44,7 @@ extern "C" {
 #endif
 
 #define CPATTN_VERSION_MAJOR 0
-#define CPATTN_VERSION_MINOR 8
+#define CPATTN_VERSION_MINOR 9
 
 typedef enum {
     CPATTN_OK = 0,
@@ -330,6 +330,18 @@ int cpattn_merge_backward(int n_parts, const float* const* o_parts, const float*
 int cpattn_sink_backward(const float* o, const float* lse, const float* sink_logits, int64_t n_heads,
                          int64_t n_rows, int64_t d, const float* g_o, float* g_o_in, float* g_lse_in,
                          float* g_sink, void* stream);
+
+/* Measurement helper, not a step of the attention path: streams `bytes` of
+ * device memory once, 16 bytes per lane and step, with `grid` workgroups of
+ * 256 lanes looping grid-stride (grid <= 0: one lane per 16 bytes, no loop).
+ * It gives the HBM-bound kernels above a bandwidth ceiling measured on the
+ * same device (the HBM3E figure of the MI355X data sheet is not reached by a
+ * plain stream).  kind 0 reads src; dst must hold 16 bytes, which are left
+ * as they are for zero-filled or random data.  kind 1 copies src to dst
+ * (the two must not overlap).  src and dst are 16-byte aligned device
+ * pointers owned by the caller; bytes is a multiple of 16, grid <= 2^20.
+ * Asynchronous on `stream`; errors as for the other calls. */
+int cpattn_stream_probe(int kind, const void* src, void* dst, int64_t bytes, int grid, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* cpattn_last_error(void);

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_error_string(L):
     import context_blockwise_attention_amd as cp
-    assert cp.version() == (0, 8)
+    assert cp.version() == (0, 9)
     assert isinstance(L.cpattn_last_error(), bytes)
 
 
@@ -122,6 +122,17 @@ def test_partial_validation(L):
     huge = _tensor(cp, n=(1 << 23), st=256)
     assert _partial(L, cp, huge, huge, huge, h) == EUNSUPPORTED                    # > 2 GiB per head
     assert L.cpattn_mask_free(h) == OK
+
+
+def test_stream_probe_validation(L):
+    """The bandwidth probe checks its arguments before any device work."""
+    assert L.cpattn_stream_probe(2, 0x1000, 0x2000, 1024, 0, None) == EINVAL      # kind
+    assert L.cpattn_stream_probe(0, 0x1000, 0x2000, 1000, 0, None) == EINVAL      # not a multiple of 16
+    assert L.cpattn_stream_probe(1, 0x1000, 0x2000, -16, 0, None) == EINVAL       # negative size
+    assert L.cpattn_stream_probe(1, 0x1000, 0x2000, 1024, 1 << 21, None) == EINVAL  # grid
+    assert L.cpattn_stream_probe(1, 0, 0x2000, 1024, 0, None) == EINVAL           # NULL
+    assert L.cpattn_stream_probe(1, 0x1008, 0x2000, 1024, 0, None) == EUNSUPPORTED  # alignment
+    assert L.cpattn_stream_probe(1, 0x1000, 0x2000, 0, 0, None) == OK             # nothing to stream
 
 
 def test_merge_and_ring_validation(L):
