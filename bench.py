@@ -531,7 +531,7 @@ def main():
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            cp.stream_probe("copy", src, dst)
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib}))
         return
