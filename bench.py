@@ -494,7 +494,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--blocks", type=int, default=4, help="ring size N (blocks of 65536/N tokens)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample: query rows per head")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample: query rows per head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing (diagnostic runs)")
     ap.add_argument("--no-balance", action="store_true",
                     help="skip the extra legs (ring sizes, zig-zag comparison, GQA, window, backward)")
