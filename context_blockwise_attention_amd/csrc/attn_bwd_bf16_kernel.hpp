@@ -574,13 +574,23 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         if (++cur_tile == n_tiles) cur_tile = 0;
         const lds_byte* qt = lds + SM::Q_OFF + slot * TT::BYTES;
         const lds_byte* dt = lds + SM::DO_OFF + slot * TT::BYTES;
+        // With a window the kernel's bookkeeping leaves no room for the 16
+        // row-read offsets the compiler would keep for the whole loop (it
+        // spilled 76 bytes per lane): the swizzle words are made opaque per
+        // tile, so each offset is recomputed next to its read (two vector
+        // instructions) and lives only there.  Without a window the kept
+        // offsets measured slightly faster.
+        BwdRowRead rrow = ro.row, rv = vread;
+        if (WIN) {
+            asm volatile("" : "+v"(rrow.x));
+            asm volatile("" : "+v"(rv.x));
+        }
 
         f32x16 s = {}, dp = {};
 #pragma unroll
         for (int ds = 0; ds < TT::DSTEPS; ++ds) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(qt + ro.row.off(ds)), kreg[ds], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(dt + ro.row.off(ds)), lds_op(lds + vread.off(ds)), dp, 0, 0,
-                                                         0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(qt + rrow.off(ds)), kreg[ds], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(dt + rrow.off(ds)), lds_op(lds + rv.off(ds)), dp, 0, 0, 0);
         }
         // lane (key jk, half g), value i: query row q0 + il, il = 16 (i / 8) + 8 g + i % 8
         const auto* lp = reinterpret_cast<const __attribute__((address_space(3))) float*>(lds + SM::L_OFF + slot * 256) + 8 * g;
