@@ -143,6 +143,98 @@ struct PPTile {
     static_assert(PF == 2, "the tile loop issues loads two iterations ahead");
 };
 
+// ---------------------------------------------------------------------------
+// Epilogue through LDS.  The same arithmetic as write_result (the partial
+// written, or merged into the running result by the stable rule), but the
+// accumulators, which a lane holds as 16-byte pieces of its own row (a wave's
+// store then touches 32 rows with 32 bytes each), are first written to an
+// 8 KB LDS area of the wave and read back row-contiguous, so that every
+// global load and store instruction covers whole 256-byte row halves.  Done
+// in passes of 64 columns.  The area's 16-byte chunks are XOR-swizzled by
+// row (conflict-free writes and reads).  Per-row factors go from the row's
+// lanes to the reading lanes by lane shuffles.  `stage` must not be touched
+// by any other wave while this runs.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void write_result_staged(const JobArgs& J, int head, int row0, int lane, const f32x16* acc,
+                                                    float m_run, float l_run, lds_byte* stage) {
+    constexpr int DBLK = D / 32;
+    constexpr int PASSES = D / 64;                // 64 columns per pass
+    const int r32 = lane & 31;
+    const int g = lane >> 5;
+    const int qi = row0 + r32;                    // this lane's accumulator row
+    const float l_tot = xhalf_sum(l_run);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse_new = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    float* const ohead = J.o + (int64_t)head * J.n_q * D;
+    float* const lhead = J.lse + (int64_t)head * J.n_q;
+    // per-row factors: out = ca * O_old + cb * acc
+    float ca = 0.f, cb = inv, lse_out = lse_new;
+    if (J.accumulate) {
+        const float lse_old = qi < J.n_q ? lhead[qi] : -INFINITY;
+        const float M = fmaxf(lse_old, lse_new);
+        const bool none = M == -INFINITY;
+        const float wa = none ? 0.f : expf(lse_old - M), wb = none ? 0.f : expf(lse_new - M);
+        const float z = wa + wb;
+        const float rz = none ? 0.f : 1.f / z;
+        ca = wa * rz;
+        cb = wb * inv * rz;
+        lse_out = none ? -INFINITY : M + logf(z);
+    }
+    // rows read back by this lane: row 4 it + lane / 16, chunk lane % 16
+    const int rsub = lane >> 4, chunk = lane & 15;
+    float ra[8], rb[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        ra[it] = __shfl(ca, it * 4 + rsub);
+        rb[it] = __shfl(cb, it * 4 + rsub);
+    }
+    auto lds4 = [&](int row, int c) {
+        return reinterpret_cast<__attribute__((address_space(3))) f32x4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+    };
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        f32x4 old[8];
+        if (J.accumulate) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int row = it * 4 + rsub;
+                old[it] = row0 + row < J.n_q
+                              ? *reinterpret_cast<const f32x4*>(ohead + (int64_t)(row0 + row) * D + ps * 64 + chunk * 4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        // accumulator blocks 2 ps, 2 ps + 1: lane (r32, g) holds columns
+        // 32 b' + 8 q4 + 4 g + e of the pass, i.e. chunk 8 b' + 2 q4 + g
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int b = 2 * ps + bb;
+                *lds4(r32, 8 * bb + 2 * q4 + g) =
+                    f32x4{acc[b][q4 * 4 + 0], acc[b][q4 * 4 + 1], acc[b][q4 * 4 + 2], acc[b][q4 * 4 + 3]};
+            }
+        // the wave's own writes are in LDS before its reads (in-order per wave)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int row = it * 4 + rsub;
+            const f32x4 a = *lds4(row, chunk);
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = J.accumulate ? ra[it] * old[it][e] + rb[it] * a[e] : rb[it] * a[e];
+            if (row0 + row < J.n_q) *reinterpret_cast<f32x4*>(ohead + (int64_t)(row0 + row) * D + ps * 64 + chunk * 4) = v;
+        }
+        // the next pass overwrites the area: every read of this one has returned
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+    }
+    if (g == 0 && qi < J.n_q) lhead[qi] = lse_out;
+    (void)DBLK;
+}
+
 template <int D, int BN_, int PF_, bool WIN>
 __global__ void __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_pp_kernel(const LaunchArgs args) {
@@ -481,6 +573,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
     // loop so that its loop-carried registers are allocated once (the G loop is
     // fully unrolled; each copy serves one group).  Every wave passes the same
     // barriers.
+    int t_last = 1;   // tiles of the walk + 1 (the epilogue's staging avoids the last V buffer)
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
         if (group != G) continue;
@@ -570,6 +663,7 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
             ++t;
         }
         // last iteration t = T: only tile T-1 (= cur) remains; nothing is left in flight
+        t_last = t;
         wait_older(0);
         phase_barrier();                                                // barrier 2T
         if (G == 0) {
@@ -584,7 +678,23 @@ attn_bf16_pp_kernel(const LaunchArgs args) {
         }
     }
 
-    write_result<D>(J, head, qi, g, acc, m_run, l_run);
+    if constexpr (TT::TILE_BYTES >= 2 * 8192) {
+        // staging areas: group 0's waves use the K buffers (free since the
+        // last S, before barrier 2T), group 1's waves the two V buffers that
+        // its last PV does not read (each wave 8 KB)
+        lds_byte* stage;
+        if (group == 0) {
+            stage = lds + TT::K_OFF + wave * 8192;
+        } else {
+            const int busy = (t_last - 1) % TT::NBUF;
+            const int f = (wave - 4) >> 1;                   // 0 or 1: the f-th V buffer other than `busy`
+            const int vb = f < busy ? f : f + 1;
+            stage = lds + TT::V_OFF + vb * TT::TILE_BYTES + ((wave - 4) & 1) * 8192;
+        }
+        write_result_staged<D>(J, head, q_first + wave * 32, lane, acc, m_run, l_run, stage);
+    } else {
+        write_result<D>(J, head, qi, g, acc, m_run, l_run);   // d 64: tiles too small to stage in
+    }
 }
 
 }  // namespace cpattn
