@@ -567,6 +567,16 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         // have landed; after the barrier every wave's have, and the other slot
         // is free
         __builtin_amdgcn_s_waitcnt(0xF70);
+        if (wave == 0) {
+            // The tile's LSEs (this wave's own load) are turned into base-2
+            // units once, +inf for rows without gradient, so that each of
+            // the 16 probabilities a lane computes per tile takes one fma
+            // instead of a multiply, a compare and a select as well (every
+            // lane of every wave reads 16 of these rows).
+            auto* lw = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + SM::L_OFF + slot * 256);
+            const float lse = lw[lane];
+            lw[lane] = lse > -INFINITY ? lse * 1.4426950408889634f : INFINITY;
+        }
         bwd_tile_barrier();
         if (step + 1 < steps) issue(slot ^ 1);
         const int entry = tile_entry(cur_tile);
@@ -574,17 +584,14 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         if (++cur_tile == n_tiles) cur_tile = 0;
         const lds_byte* qt = lds + SM::Q_OFF + slot * TT::BYTES;
         const lds_byte* dt = lds + SM::DO_OFF + slot * TT::BYTES;
-        // With a window the kernel's bookkeeping leaves no room for the 16
-        // row-read offsets the compiler would keep for the whole loop (it
-        // spilled 76 bytes per lane): the swizzle words are made opaque per
-        // tile, so each offset is recomputed next to its read (two vector
-        // instructions) and lives only there.  Without a window the kept
-        // offsets measured slightly faster.
+        // The kernel has no room for the 16 row-read offsets the compiler
+        // would keep for the whole loop (it spilled up to 76 bytes per lane):
+        // the swizzle words are made opaque per tile, so each offset is
+        // recomputed next to its read (two vector instructions) and lives
+        // only there.
         BwdRowRead rrow = ro.row, rv = vread;
-        if (WIN) {
-            asm volatile("" : "+v"(rrow.x));
-            asm volatile("" : "+v"(rv.x));
-        }
+        asm volatile("" : "+v"(rrow.x));
+        asm volatile("" : "+v"(rv.x));
 
         f32x16 s = {}, dp = {};
 #pragma unroll
@@ -605,11 +612,7 @@ attn_bwd_dkv_bf16_kernel(const BwdArgs args) {
         const auto* lqp = reinterpret_cast<const __attribute__((address_space(3))) int*>(lds + SM::LQ_OFF + slot * 256) + 8 * g;
         bf16x8 pb[2], dsb[2];
         // a row without gradient (LSE = -inf) gets p = 0
-        auto prob = [&](int i, int il) {
-            const float lse = lp[il];
-            const float l2 = lse > -INFINITY ? lse * 1.4426950408889634f : INFINITY;
-            return __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l2));
-        };
+        auto prob = [&](int i, int il) { return __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lp[il])); };
         if (full) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
