@@ -100,6 +100,15 @@ struct LaunchArgs {
 // after another, the group's q-tiles heaviest (last) first, so the ~32
 // workgroups in flight on the XCD read the same head's K/V and share its L2.
 // With fewer heads the same group order is dealt round-robin over the XCDs.
+// An XCD starts its workgroups strictly in order and deals them round-robin
+// over its four shader engines (measured with per-workgroup hardware ids), so
+// slot p and slot p + 4 land on the same engine.  With q-tiles in plain
+// descending order one engine would always get the heaviest of every four
+// and fall behind, and the in-order dealer would hold the other engines' free
+// CUs waiting for it (on the diagonal launch of the 64K row 5% of the CU time
+// went to such gaps).  So the second half of every block of eight is
+// reversed: slots p and p + 4 then hold tiles whose weights (linear in the
+// q-tile on a causal diagonal) sum to the same value in every block.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool work_item(const LaunchArgs& a, int bid, int* job, int* head, int* qtile) {
     const bool by_xcd = a.heads_per_xcd > 0;
@@ -121,7 +130,8 @@ __device__ __forceinline__ bool work_item(const LaunchArgs& a, int bid, int* job
             if (h >= a.heads) return false;
             *job = j;
             *head = h;
-            *qtile = qt - 1 - r;
+            const int rb = ((r & 4) && (r | 7) < qt) ? (r ^ 3) : r;   // complete blocks of 8 only
+            *qtile = qt - 1 - rb;
             return true;
         }
         p -= n;
