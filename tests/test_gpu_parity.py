@@ -96,6 +96,21 @@ def test_partial_causal(cp, dtype, d, nq, nk, qbase, kbase):
     _cmp(o, l, O, L, dtype, "causal partial")
 
 
+@pytest.mark.parametrize("H,nq", [(2, 2900), (9, 2600)])
+def test_partial_causal_qtile_blocks(cp, H, nq):
+    """More than eight 256-row query tiles in a count that is not a multiple
+    of eight: the workgroups take a job's q-tiles in blocks of eight with the
+    second half reversed, and a trailing partial block keeps its order.  With
+    2 heads (fewer than the XCDs) and 9 (two head slots per XCD, some of them
+    empty).  Every row against the oracle."""
+    d = 128
+    q, k, v = workloads.qkv(4, H, nq, d, "bf16")
+    mask = cp.Mask.causal(nq)
+    o, l = cp.partial(_dev(q), _dev(k), _dev(v), mask, (0, 1), (0, 1))
+    O, L = oracle.attention(q, k, v, np.arange(nq), np.arange(nq), oracle.Causal())
+    _cmp(o, l, O, L, "bf16", "causal partial, %d heads x %d rows" % (H, nq))
+
+
 @pytest.mark.parametrize("P", [2, 4])
 def test_partial_striped(cp, P):
     H, n, d = 2, 1200, 128
