@@ -158,7 +158,6 @@ struct PPTile {
 template <int D>
 __device__ __forceinline__ void write_result_staged(const JobArgs& J, int head, int row0, int lane, const f32x16* acc,
                                                     float m_run, float l_run, lds_byte* stage) {
-    constexpr int DBLK = D / 32;
     constexpr int PASSES = D / 64;                // 64 columns per pass
     const int r32 = lane & 31;
     const int g = lane >> 5;
@@ -232,7 +231,6 @@ __device__ __forceinline__ void write_result_staged(const JobArgs& J, int head, 
         asm volatile("" ::: "memory");
     }
     if (g == 0 && qi < J.n_q) lhead[qi] = lse_out;
-    (void)DBLK;
 }
 
 template <int D, int BN_, int PF_, bool WIN>
