@@ -7,9 +7,11 @@
   times, with eager work between the replays (the outputs overwritten by
   fill kernels), gives the eager result bit for bit on every replay: the
   calls enqueue only kernels, no allocation, copy or memset.
+* The same for the ring backward (dQ, dK, dV added into the caller's
+  buffers, which are zeroed before each replay).
 
-The forward kernels are deterministic (fixed reduction order, no atomics), so
-equal inputs give equal bits.
+The kernels are deterministic (fixed reduction order and launch order, no
+atomics), so equal inputs give equal bits.
 """
 import pytest
 import torch
@@ -95,3 +97,67 @@ def test_graph_capture_replay(cp):
         _same(out_g, ref, "replay %d" % rep)
     del g
     mask.free()
+
+
+def _backward_inputs(cp, Q, K, V, pos, mask, outs, seed):
+    cur = torch.cuda.current_stream()
+    fwd = cp.ring_emulate(Q, K, V, pos, mask, outs=outs(), stream=cur)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    douts = [torch.randn(q.shape, generator=g).to(torch.bfloat16).to(q.device) for q in Q]
+    deltas = [cp.backward_delta(fwd[r][0], douts[r]) for r in range(len(Q))]
+    lses = [fwd[r][1] for r in range(len(Q))]
+    zeros = lambda: [tuple(torch.zeros(t.shape, dtype=torch.float32, device=t.device) for t in (Q[r], K[r], V[r]))
+                     for r in range(len(Q))]
+    return lses, deltas, douts, zeros
+
+
+def _same_grads(a, b, what):
+    for r, (ga, gb) in enumerate(zip(a, b)):
+        for x, y, name in zip(ga, gb, ("dQ", "dK", "dV")):
+            assert torch.equal(x, y), "%s: rank %d %s differs (max |diff| %.3g)" % (
+                what, r, name, float((x - y).abs().max()))
+
+
+def test_backward_two_streams_and_graph_replay(cp):
+    """The ring backward (dQ, dK, dV added into the caller's buffers) on two
+    streams at once next to a second problem's, and captured in a graph and
+    replayed (buffers zeroed by eager fill kernels before each replay): bit
+    for bit the eager result every time."""
+    A = _problem(cp, 21, 8, 2048, (1024,) * 3, 4)
+    B = _problem(cp, 22, 4, 1024, (512,) * 6, 3)
+    la, da, ga, za = _backward_inputs(cp, *A, seed=5)
+    lb, db, gb, zb = _backward_inputs(cp, *B, seed=6)
+    cur = torch.cuda.current_stream()
+    ref_a = cp.ring_backward(*A[:5], la, da, ga, grads=za(), stream=cur)
+    ref_b = cp.ring_backward(*B[:5], lb, db, gb, grads=zb(), stream=cur)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(cur)
+    s2.wait_stream(cur)
+    out_a, out_b = za(), zb()
+    cp.ring_backward(*A[:5], la, da, ga, grads=out_a, stream=s1)
+    cp.ring_backward(*B[:5], lb, db, gb, grads=out_b, stream=s2)
+    torch.cuda.synchronize()
+    _same_grads(out_a, ref_a, "stream 1")
+    _same_grads(out_b, ref_b, "stream 2")
+
+    grads = za()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        cp.ring_backward(*A[:5], la, da, ga, grads=grads)   # warm-up before capture
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cp.ring_backward(*A[:5], la, da, ga, grads=grads)
+    for rep in range(3):
+        for trio in grads:
+            for t in trio:
+                t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same_grads(grads, ref_a, "replay %d" % rep)
+    del graph
+    A[4].free()
+    B[4].free()
