@@ -242,18 +242,11 @@ def gqa_ring(cp, workloads, torch, dev, seg, parent, N, flops, steps: int = 10):
     outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
                 torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
     stream = torch.cuda.current_stream()
-    for _ in range(2):
-        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, wall = _timed(torch, stream, lambda: cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream), steps)
     mask.free()
     return {"workload": "tree64k ring of %d, 32 query heads over 4 K/V heads, d 128, bf16" % N,
-            "ms_per_step": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall, 4),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
@@ -273,15 +266,7 @@ def window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N, window: i
     outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
                 torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
     stream = torch.cuda.current_stream()
-    for _ in range(2):
-        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, wall = _timed(torch, stream, lambda: cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream), steps)
     # the same ring's backward (10 d FLOPs per visible pair, as the headline's)
     g = torch.Generator(device="cpu").manual_seed(8)
     douts = [x.contiguous() for x in blk(torch.randn((H, n, d), generator=g).to(torch.bfloat16).to(dev))]
@@ -294,21 +279,15 @@ def window_ring(cp, workloads, torch, dev, qd, kd, vd, seg, parent, N, window: i
         cp.ring_backward(Q, K, V, pos, mask, [outs[r][1] for r in range(N)], deltas, douts, grads=grads,
                          stream=stream)
 
-    bstep()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(3):
-        bstep()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    bms = e0.elapsed_time(e1) / 3
+    bms, bwall = _timed(torch, stream, bstep, 3, warmup=1)
     bflops = 2.5 * flops
     mask.free()
     return {"workload": "tree64k ring of %d, sliding window of %d logical positions" % (N, window),
-            "visible_pairs_per_head": pairs, "ms_per_step": round(ms, 4),
+            "visible_pairs_per_head": pairs, "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall, 4),
             "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "backward": {"ms_per_step": round(bms, 4), "TFLOP/s": round(bflops / (bms * 1e-3) / 1e12, 2),
+            "backward": {"ms_per_step": round(bms, 4), "wall_ms_per_step": round(bwall, 4),
+                         "TFLOP/s": round(bflops / (bms * 1e-3) / 1e12, 2),
                          "frac_of_bf16_peak": round(bflops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
 
 
@@ -335,19 +314,12 @@ def backward_ring(cp, torch, dev, qd, kd, vd, seg, parent, N, outs, A, steps: in
         cp.ring_backward(blk(qd), blk(kd), blk(vd), pos, mask, [outs[r][1] for r in range(N)], deltas, douts,
                          grads=grads, stream=stream)
 
-    step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, wall = _timed(torch, stream, step, steps, warmup=1)
     mask.free()
     flops = 10.0 * d * H * A
     return {"workload": "tree64k ring of %d, backward (dQ, dK, dV) with the complete O and LSE" % N,
-            "ms_per_step": round(ms, 4), "flops_convention": "10 d per visible pair and head (2.5x forward)",
+            "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall, 4),
+            "flops_convention": "10 d per visible pair and head (2.5x forward)",
             "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
@@ -499,9 +471,11 @@ def ring_sizes(cp, torch, dev, qd, kd, vd, mask, seg, parent, flops, sizes=(1, 8
         pos = [(r * c, 1) for r in range(N)]
         outs = {r: (torch.empty((H, c, d), dtype=torch.float32, device=dev),
                     torch.empty((H, c), dtype=torch.float32, device=dev)) for r in range(N)}
-        ms = _time_reps(torch, stream, steps, lambda: cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream))
+        ms, wall = _timed(torch, stream, lambda: cp.ring_emulate(Q, K, V, pos, mask, outs=outs, stream=stream),
+                          steps, warmup=max(10, steps))
         launches = int((block_pair_counts(seg, parent, c, N) > 0).sum(axis=1).max())
         out["N%d" % N] = {"blocks": N, "block_tokens": c, "launches": launches, "ms_per_step": round(ms, 4),
+                          "wall_ms_per_step": round(wall, 4),
                           "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
                           "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del outs
