@@ -219,6 +219,31 @@ def test_partial_backward_gqa(cp, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_partial_backward_gqa_window(cp, dtype):
+    """Grouped-query heads and a sliding window on a tree, backward."""
+    H, hkv, n, d, window = 8, 2, 260, 128, 70
+    g = H // hkv
+    q, _, _ = workloads.qkv(57, H, n, d, dtype)
+    _, k, v = workloads.qkv(58, hkv, n, d, dtype)
+    G = _grad_out(59, H, n, d, dtype)
+    seg, parent = workloads.tree_prompt_completions(100, (60, 100))
+    mask = cp.Mask.tree(seg, parent).with_window(window)
+    omask = oracle.Tree(seg, parent, window=window)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    o, l = cp.partial(qd, kd, vd, mask)
+    delta = cp.backward_delta(o, gd)
+    dq, dk, dv = cp.partial_backward(qd, kd, vd, mask, l, delta, gd)
+    torch.cuda.synchronize()
+    pos = np.arange(n)
+    kr, vr = k.repeat_interleave(g, 0), v.repeat_interleave(g, 0)
+    O, L = oracle.attention(q, kr, vr, pos, pos, omask)
+    rq, rk, rv = oracle.attention_backward(q, kr, vr, pos, pos, O, L, G.double().numpy(), omask)
+    _check("dq", dq, rq, dtype)
+    _check("dk", dk, rk.reshape(hkv, g, n, d).sum(1), dtype)
+    _check("dv", dv, rv.reshape(hkv, g, n, d).sum(1), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ring_backward_tree(cp, dtype):
     N, H, d = 4, 2, 128
     seg, parent = workloads.tree_prompt_completions(384, (128, 200, 96, 160))

@@ -5,7 +5,8 @@ The reference reduces GQA to multi-head attention with every K/V head
 repeated g times (brute force), so the fp64 oracle needs no GQA code.
 
 * partial attention, H = 8 query heads over 2 and 1 K/V heads, causal and
-  tree, bf16 and fp32, every row (tolerances as for multi-head);
+  tree, bf16 and fp32, every row (tolerances as for multi-head), also with a
+  sliding window;
 * the 64K tree row, ring of 4, 32 query / 4 KV heads: bitwise equal to the
   same ring with the K/V heads materialised 8 times (the kernels do the same
   arithmetic on the same values), and sampled rows of 8 heads against the
@@ -53,6 +54,28 @@ def test_partial_gqa(cp, dtype, hkv, maskname):
     pos = np.arange(n)
     O_ref, L_ref = oracle.attention(q, _repeat_heads(k, g), _repeat_heads(v, g), pos, pos, omask)
     _cmp(o, l, O_ref, L_ref, dtype, "gqa %s %s hkv=%d" % (dtype, maskname, hkv))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("maskname,window", [("causal", 45), ("tree", 30), ("tree", 120)])
+def test_partial_gqa_window(cp, dtype, maskname, window):
+    """Grouped-query heads with a sliding window (on logical positions for
+    the tree): the K/V head index and the window mask are independent parts
+    of the kernel, checked together."""
+    H, hkv, n, d = 8, 2, 300, 128
+    g = H // hkv
+    q, _, _ = workloads.qkv(7, H, n, d, dtype)
+    _, k, v = workloads.qkv(8, hkv, n, d, dtype)
+    if maskname == "causal":
+        mask, omask = cp.Mask.causal(n).with_window(window), oracle.Causal(window=window)
+    else:
+        seg, parent = workloads.tree_prompt_completions(100, (80, 70, 50))
+        mask, omask = cp.Mask.tree(seg, parent).with_window(window), oracle.Tree(seg, parent, window=window)
+    o, l = cp.partial(q.cuda(), k.cuda(), v.cuda(), mask)
+    torch.cuda.synchronize()
+    pos = np.arange(n)
+    O_ref, L_ref = oracle.attention(q, _repeat_heads(k, g), _repeat_heads(v, g), pos, pos, omask)
+    _cmp(o, l, O_ref, L_ref, dtype, "gqa window %s %s W=%d" % (dtype, maskname, window))
 
 
 def test_tree64k_ring_gqa_32q_4kv(cp):
