@@ -305,6 +305,45 @@ def test_zigzag_ring_backward(cp, dtype, maskname):
         _check(name, got, ref, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zigzag_ring_backward_gqa(cp, dtype):
+    """Zig-zag chunks with grouped-query heads (4 query heads over 2 K/V
+    heads) on a packed tree, backward: dK/dV of a K/V head sum its group's
+    query heads."""
+    N, H, hkv, d = 4, 4, 2, 128
+    g = H // hkv
+    seg, parent = workloads.tree_prompt_completions(320, (160, 200, 88))
+    n = len(seg)
+    mask, omask = cp.Mask.tree(seg, parent), oracle.Tree(seg, parent)
+    c = n // (2 * N)
+    q, _, _ = workloads.qkv(72, H, n, d, dtype)
+    _, k, v = workloads.qkv(73, hkv, n, d, dtype)
+    G = _grad_out(74, H, n, d, dtype)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    chunks = [ch for r in range(N) for ch in (r, 2 * N - 1 - r)]
+    cut = lambda t: [t[:, ch * c:(ch + 1) * c].contiguous() for ch in chunks]
+    pos = [(ch * c, 1) for ch in chunks]
+    Q, K, V, Gs = cut(qd), cut(kd), cut(vd), cut(gd)
+    out = cp.ring_emulate_chunks(Q, K, V, pos, mask, chunks_per_rank=2)
+    deltas = [cp.backward_delta(out[i][0], Gs[i]) for i in range(2 * N)]
+    grads = cp.ring_backward_chunks(Q, K, V, pos, mask, [out[i][1] for i in range(2 * N)], deltas, Gs,
+                                    chunks_per_rank=2)
+    torch.cuda.synchronize()
+    m = 2 * N * c
+    allpos = np.arange(m)
+    kr, vr = k[:, :m].repeat_interleave(g, 0), v[:, :m].repeat_interleave(g, 0)
+    O, L = oracle.attention(q[:, :m], kr, vr, allpos, allpos, omask)
+    rq, rk, rv = oracle.attention_backward(q[:, :m], kr, vr, allpos, allpos, O, L, G[:, :m].double().numpy(), omask)
+    refs = (rq, rk.reshape(hkv, g, m, d).sum(1), rv.reshape(hkv, g, m, d).sum(1))
+    for name, j in (("dq", 0), ("dk", 1), ("dv", 2)):
+        heads = H if j == 0 else hkv
+        got = torch.zeros((heads, m, d), dtype=torch.float64)
+        for i, ch in enumerate(chunks):
+            got[:, ch * c:(ch + 1) * c] = grads[i][j].double().cpu()
+        _check(name, got, refs[j], dtype)
+    mask.free()
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("window", [0, 40, 170])
 def test_random_tree_backward(cp, seed, window):

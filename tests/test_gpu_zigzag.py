@@ -108,6 +108,31 @@ def test_tree_zigzag_equals_contiguous(cp):
     assert float((Oz - Oc).abs().max()) <= 2e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tree_zigzag_gqa(cp, dtype):
+    """Zig-zag chunks with grouped-query heads (8 query heads over 2 K/V
+    heads) on a packed tree, every row against the reference with the K/V
+    heads repeated."""
+    H, hkv, d, N = 8, 2, 128, 4
+    g = H // hkv
+    seg, parent = workloads.tree_prompt_completions(384, (256, 192, 192))
+    n = len(seg)
+    q, _, _ = workloads.qkv(9, H, n, d, dtype)
+    _, k, v = workloads.qkv(10, hkv, n, d, dtype)
+    mask = cp.Mask.tree(seg, parent)
+    O, L = _zigzag_ring(cp, q.cuda(), k.cuda(), v.cuda(), N, mask)
+    torch.cuda.synchronize()
+    pos = np.arange(n)
+    Oref, Lref = oracle.attention(q, k.repeat_interleave(g, 0), v.repeat_interleave(g, 0), pos, pos,
+                                  oracle.Tree(seg, parent))
+    do = float(np.abs(O.double().cpu().numpy() - Oref).max())
+    dl = float(np.abs(L.double().cpu().numpy() - Lref).max())
+    _print("tree zig-zag gqa %s: max|dO| %.2e max|dLSE| %.2e" % (dtype, do, dl))
+    tol_o, tol_l = (1e-5, 1e-5) if dtype == "f32" else (2e-2, 1e-3)
+    assert do <= tol_o and dl <= tol_l
+    mask.free()
+
+
 def _dense_tree_visibility(seg, parent):
     """vis[y, x]: key x visible to query y, from the trajectories: x's segment
     is y's segment (and x <= y) or a strict ancestor of it."""
