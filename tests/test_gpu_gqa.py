@@ -78,6 +78,23 @@ def test_partial_gqa_window(cp, dtype, maskname, window):
     _cmp(o, l, O_ref, L_ref, dtype, "gqa window %s %s W=%d" % (dtype, maskname, window))
 
 
+@pytest.mark.parametrize("b", [0, 1])
+def test_partial_striped_gqa(cp, b):
+    """Striped positions (P = 2, rank 0's queries against stripe b) with 8
+    query heads over 2 K/V heads."""
+    H, hkv, n, d, P = 8, 2, 400, 128, 2
+    g = H // hkv
+    q, _, _ = workloads.qkv(11, H, n * P, d, "bf16")
+    _, k, v = workloads.qkv(12, hkv, n * P, d, "bf16")
+    lay = workloads.striped(n * P, P)
+    mask = cp.Mask.causal(n * P)
+    qq, kk, vv = q[:, lay[0]], k[:, lay[b]], v[:, lay[b]]
+    o, l = cp.partial(qq.cuda(), kk.cuda(), vv.cuda(), mask, (0, P), (b, P))
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(qq, _repeat_heads(kk, g), _repeat_heads(vv, g), lay[0], lay[b], oracle.Causal())
+    _cmp(o, l, O_ref, L_ref, "bf16", "striped gqa stripe %d" % b)
+
+
 def test_tree64k_ring_gqa_32q_4kv(cp):
     H, hkv, d, N = 32, 4, 128, 4
     g = H // hkv
