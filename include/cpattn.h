@@ -23,7 +23,12 @@
  *  - Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
  *    Compute calls validate their arguments synchronously, then enqueue work
  *    on the stream and return without waiting.  A launch failure returns
- *    CPATTN_EDEVICE with the HIP error text.
+ *    CPATTN_EDEVICE with the HIP error text.  Compute calls enqueue kernels
+ *    only (no allocation, copy, memset or synchronisation), so they may be
+ *    captured in a HIP graph, and calls on different streams share no state;
+ *    the kernels are deterministic, so equal inputs give equal bits.  Mask
+ *    constructors copy and synchronise on their stream and are not for
+ *    capture.
  *  - Fail fast: unsupported combinations return CPATTN_EUNSUPPORTED; nothing
  *    falls back to another code path.
  *  - Extents (token counts, head counts, block counts, tree shapes) are
