@@ -84,6 +84,61 @@ def test_static_descriptor_two_calls(cp):
     _check_case(cp, seg2, parent2, 1, 256)
 
 
+def _random_preorder_tree(seed, n_seg, seg_len):
+    """A random rooted tree of n_seg segments (each segment's parent drawn
+    uniformly from the earlier ones), relabelled in depth-first preorder and
+    packed with seg_len tokens per segment."""
+    rng = np.random.default_rng(seed)
+    parent = np.concatenate([[-1], rng.integers(0, np.arange(1, n_seg))])
+    kids = [[] for _ in range(n_seg)]
+    for s_, p_ in enumerate(parent[1:], 1):
+        kids[p_].append(s_)
+    order, stack = [], [0]
+    while stack:
+        s_ = stack.pop()
+        order.append(s_)
+        stack.extend(reversed(kids[s_]))
+    new = np.empty(n_seg, dtype=np.int64)
+    new[np.asarray(order)] = np.arange(n_seg)
+    par = [-1 if parent[s_] < 0 else int(new[parent[s_]]) for s_ in order]
+    return workloads.tree_from_lengths([seg_len] * n_seg, par)
+
+
+def test_static_descriptor_at_its_limits(cp):
+    """The largest tree the static buffer holds: CPATTN_STATIC_MAX_TOK tokens
+    in CPATTN_STATIC_MAX_SEG segments (a random preorder tree of 65536
+    segments of 16 tokens, depth about 25).  The ring of 4 over it (2 heads,
+    d 64, bf16) gives the allocated descriptor's outputs bit for bit, and
+    sampled rows (every head, the first and last row of some segments among
+    them) match the fp64 reference."""
+    n_seg, seg_len = 1 << 16, 16
+    seg, parent = _random_preorder_tree(5, n_seg, seg_len)
+    n = len(seg)
+    assert n == 1 << 20
+    H, d, N = 2, 64, 4
+    q, k, v = workloads.qkv(7, H, n, d, "bf16")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ref_mask = cp.Mask.tree(seg, parent)
+    o_ref, l_ref = _ring(cp, qd, kd, vd, N, ref_mask)
+    st_mask = cp.Mask.tree_static(seg, parent)
+    assert st_mask.n_pos == n
+    o_st, l_st = _ring(cp, qd, kd, vd, N, st_mask)
+    assert torch.equal(o_st, o_ref) and torch.equal(l_st, l_ref), "static descriptor gives other outputs"
+    pos = np.arange(n)
+    firsts = np.arange(0, n, seg_len)
+    for h in range(H):
+        forced = np.concatenate([firsts[::4096], firsts[::4096] + seg_len - 1, [n - 1]])
+        rows = workloads.sample_rows(11, h, n, forced=forced, count=96)
+        O, L = oracle.attention(q[h:h + 1], k[h:h + 1], v[h:h + 1], pos, pos, oracle.Tree(seg, parent), rows=rows)
+        idx = torch.from_numpy(rows).cuda()
+        do = float(np.abs(o_st[h].index_select(0, idx).double().cpu().numpy() - O[0]).max())
+        dl = float(np.abs(l_st[h].index_select(0, idx).double().cpu().numpy() - L[0]).max())
+        print("  head %d: %d rows, max|dO| %.2e max|dLSE| %.2e" % (h, len(rows), do, dl), flush=True)
+        assert do <= 2e-2 and dl <= 1e-3
+    st_mask.free()
+    ref_mask.free()
+
+
 @pytest.mark.parametrize("seg,parent,code", [
     ([0, 0, 1, 1, 2, 2], [-1, -1, 0], -2),   # child stored outside its parent's subtree
     ([0, 1, 0], [-1, 0], -1),                # segment 0 split into two runs
