@@ -19,7 +19,8 @@ only itself, p = 1 and dS = dot(dO, v) - D = 0 up to fp32 rounding).
 * striped position maps (stride 4), with and without a window, every pair of
   stripes against the complete forward's (O, L);
 * the zig-zag (chunked) ring backward (N = 4, two chunks per rank), causal
-  and packed tree, every element;
+  and packed tree, also with grouped-query heads and with sliding windows,
+  every element;
 * random preorder trees (nested segments, ragged lengths), with and without
   windows, split into unequal key/query blocks, every element;
 * a windowed prompt with 80 completions, whose key blocks see more query
@@ -303,6 +304,47 @@ def test_zigzag_ring_backward(cp, dtype, maskname):
         for i, ch in enumerate(chunks):
             got[:, ch * c:(ch + 1) * c] = grads[i][j].double().cpu()
         _check(name, got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("maskname,window", [("causal", 70), ("tree", 40), ("tree", 150)])
+def test_zigzag_ring_backward_window(cp, dtype, maskname, window):
+    """Zig-zag chunks (rank r holds chunks r and 2N-1-r) with a sliding window
+    on logical positions, backward: the chunk pairs that the window empties
+    are skipped, the rest go through the windowed dQ and dK/dV kernels."""
+    N, H, d = 4, 2, 128
+    if maskname == "causal":
+        n = 8 * 96
+        mask, omask = cp.Mask.causal(n).with_window(window), oracle.Causal(window=window)
+    else:
+        seg, parent = workloads.tree_prompt_completions(320, (160, 200, 88))
+        n = len(seg)
+        mask = cp.Mask.tree(seg, parent).with_window(window)
+        omask = oracle.Tree(seg, parent, window=window)
+    c = n // (2 * N)
+    m = 2 * N * c
+    q, k, v = workloads.qkv(75, H, n, d, dtype)
+    G = _grad_out(76, H, n, d, dtype)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), G.cuda()
+    chunks = [ch for r in range(N) for ch in (r, 2 * N - 1 - r)]
+    cut = lambda t: [t[:, ch * c:(ch + 1) * c].contiguous() for ch in chunks]
+    pos = [(ch * c, 1) for ch in chunks]
+    Q, K, V, Gs = cut(qd), cut(kd), cut(vd), cut(gd)
+    out = cp.ring_emulate_chunks(Q, K, V, pos, mask, chunks_per_rank=2)
+    deltas = [cp.backward_delta(out[i][0], Gs[i]) for i in range(2 * N)]
+    grads = cp.ring_backward_chunks(Q, K, V, pos, mask, [out[i][1] for i in range(2 * N)], deltas, Gs,
+                                    chunks_per_rank=2)
+    torch.cuda.synchronize()
+    allpos = np.arange(m)
+    O, L = oracle.attention(q[:, :m], k[:, :m], v[:, :m], allpos, allpos, omask)
+    rq, rk, rv = oracle.attention_backward(q[:, :m], k[:, :m], v[:, :m], allpos, allpos, O, L,
+                                           G[:, :m].double().numpy(), omask)
+    for name, j, ref in (("dq", 0, rq), ("dk", 1, rk), ("dv", 2, rv)):
+        got = torch.zeros((H, m, d), dtype=torch.float64)
+        for i, ch in enumerate(chunks):
+            got[:, ch * c:(ch + 1) * c] = grads[i][j].double().cpu()
+        _check(name, got, ref, dtype)
+    mask.free()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
