@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -399,18 +400,30 @@ static double pair_estimate(const cpattn_mask* m, cpattn_posmap qp, int64_t nq, 
 // ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
+// Raises a kernel's dynamic LDS limit to `bytes` once per device, before its
+// first launch there.  `done` is the kernel's set of devices already raised
+// (bit d: device d); host threads may race here, which is harmless: the call
+// is idempotent, and a device is marked only after it succeeded.  Devices
+// past 63 are raised on every launch.
+static hipError_t raise_lds_limit(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 template <typename T, int D, int BN, bool WIN>
 static int launch_partial_t(LaunchArgs& a, hipStream_t st) {
     using TL = Tile<T, D, BN>;
     const int smem = 2 * TL::STAGE_BYTES;
     const auto kern = partial_attention_kernel<T, D, BN, WIN>;
-    static bool attr_set = false;   // per instantiation; the attribute is per function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_raised{0};   // per instantiation: the attribute is per function
+    if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), smem, lds_raised); e != hipSuccess)
+        return hip_fail(e, "hipFuncSetAttribute");
     const int grid = (a.total_wg + 7) / 8 * 8;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, st, a);
     hipError_t e = hipGetLastError();
@@ -428,13 +441,9 @@ static int launch_bf16(LaunchArgs& a, hipStream_t st) {
     using TT = PPTile<D, kBf16BN, kBf16PF>;
     const auto kern = attn_bf16_pp_kernel<D, kBf16BN, kBf16PF, WIN>;
     const int smem = WIN ? TT::LDS_BYTES_WIN : TT::LDS_BYTES;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_raised{0};
+    if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), smem, lds_raised); e != hipSuccess)
+        return hip_fail(e, "hipFuncSetAttribute");
     const int grid = (a.total_wg + 7) / 8 * 8;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kPPThreads), smem, st, a);
     hipError_t e = hipGetLastError();
@@ -907,16 +916,10 @@ static int launch_bwd_t(BwdArgs& a, bool dkv, hipStream_t st) {
         smem_dq = (2 * S::ROW_ELEMS + S::T_ELEMS) * (int)sizeof(T) + 2 * kBwdTile * 4;
         smem_dkv = (2 * S::ROW_ELEMS + 2 * S::T_ELEMS) * (int)sizeof(T) + 3 * kBwdTile * 4;
     }
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kq),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem_dq);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kkv), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    smem_dkv);
-        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> raised_dq{0}, raised_dkv{0};
+    hipError_t ea = raise_lds_limit(reinterpret_cast<const void*>(kq), smem_dq, raised_dq);
+    if (ea == hipSuccess) ea = raise_lds_limit(reinterpret_cast<const void*>(kkv), smem_dkv, raised_dkv);
+    if (ea != hipSuccess) return hip_fail(ea, "hipFuncSetAttribute");
     if (a.total_wg == 0) return CPATTN_OK;
     if (dkv) hipLaunchKernelGGL(kkv, dim3(a.total_wg), dim3(kBwdThreads), smem_dkv, st, a);
     else hipLaunchKernelGGL(kq, dim3(a.total_wg), dim3(kBwdThreads), smem_dq, st, a);
