@@ -214,3 +214,24 @@ def test_merge_kernel_shapes(cp, n_parts, d):
     # the output may alias part 0 (documented in-place use)
     cp.merge(dev, out=dev[0])
     _cmp(dev[0][0], dev[0][1], Om, Lm, "f32", "in-place merge of %d parts, d %d" % (n_parts, d))
+
+
+def test_merge_kernel_misaligned_parts(cp):
+    """Parts and output at a 4-byte offset from a 16-byte boundary (contiguous
+    tensors that start one float into their storage), d a multiple of 4: the
+    kernel takes its one-float path instead of 16-byte units."""
+    n_parts, rows, d = 3, 45, 128
+    parts = _merge_parts(n_parts, rows, d, 7)
+    Om, Lm = oracle.merge([(a.astype(np.float64), b.astype(np.float64)) for a, b in parts])
+
+    def shifted(a):
+        buf = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+        t = buf[1:].view(a.shape)
+        t.copy_(torch.from_numpy(a))
+        assert t.is_contiguous() and t.data_ptr() % 16 == 4
+        return t
+
+    dev = [(shifted(a), torch.from_numpy(b).cuda()) for a, b in parts]
+    out = (shifted(np.zeros((3, rows, d), dtype=np.float32)), torch.empty((3, rows), device="cuda"))
+    o, l = cp.merge(dev, out=out)
+    _cmp(o, l, Om, Lm, "f32", "merge of misaligned parts")
