@@ -25,6 +25,7 @@ Entry points (same names as the C ABI):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -120,6 +121,21 @@ def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _on(stream):
+    """Context for the tensors a call allocates itself (outputs, zero-filled
+    gradient buffers): made on the stream the call enqueues on.  torch's
+    caching allocator ties a block to the stream it is made on, and a zero
+    fill runs on that stream, so both are then ordered with the call's
+    kernels; made on another stream, a fill could still be running when the
+    kernels add into the buffer."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        handle = int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+        stream = torch.cuda.default_stream() if handle == 0 else torch.cuda.ExternalStream(handle)
+    return torch.cuda.stream(stream)
 
 
 def _desc(t: Optional[torch.Tensor], name: str) -> _Tensor:
@@ -233,8 +249,9 @@ def partial(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, q_pos
     if out is None:
         if accumulate:
             raise ValueError("accumulate needs out=")
-        out = (torch.empty((H, nq, d), dtype=torch.float32, device=q.device),
-               torch.empty((H, nq), dtype=torch.float32, device=q.device))
+        with _on(stream):
+            out = (torch.empty((H, nq, d), dtype=torch.float32, device=q.device),
+                   torch.empty((H, nq), dtype=torch.float32, device=q.device))
     o, lse = out
     if o.shape != (H, nq, d) or lse.shape != (H, nq) or o.dtype != torch.float32 or lse.dtype != torch.float32 \
             or not o.is_contiguous() or not lse.is_contiguous():
@@ -263,7 +280,8 @@ def merge(parts: Sequence[Tuple[torch.Tensor, torch.Tensor]], out=None, stream=N
         if o.numel() != rows * d:
             raise ValueError("O and LSE shapes disagree")
     if out is None:
-        out = (torch.empty_like(o0), torch.empty_like(l0))
+        with _on(stream):
+            out = (torch.empty_like(o0), torch.empty_like(l0))
     n = len(parts)
     optrs = (ctypes.c_void_p * n)(*[p[0].data_ptr() for p in parts])
     lptrs = (ctypes.c_void_p * n)(*[p[1].data_ptr() for p in parts])
@@ -288,8 +306,9 @@ def ring_emulate(q_blocks: Sequence[Optional[torch.Tensor]], k_blocks: Sequence[
         outs = {}
         for r in run:
             nq = q_blocks[r].shape[1]
-            outs[r] = (torch.empty((H, nq, d), dtype=torch.float32, device=k_blocks[0].device),
-                       torch.empty((H, nq), dtype=torch.float32, device=k_blocks[0].device))
+            with _on(stream):
+                outs[r] = (torch.empty((H, nq, d), dtype=torch.float32, device=k_blocks[0].device),
+                           torch.empty((H, nq), dtype=torch.float32, device=k_blocks[0].device))
     for r in run:
         o, l = outs[r]
         nq = q_blocks[r].shape[1]
@@ -334,8 +353,9 @@ def ring_emulate_chunks(q_chunks: Sequence[Optional[torch.Tensor]], k_chunks: Se
         outs = {}
         for i in units:
             nq = q_chunks[i].shape[1]
-            outs[i] = (torch.empty((H, nq, d), dtype=torch.float32, device=k_chunks[0].device),
-                       torch.empty((H, nq), dtype=torch.float32, device=k_chunks[0].device))
+            with _on(stream):
+                outs[i] = (torch.empty((H, nq, d), dtype=torch.float32, device=k_chunks[0].device),
+                           torch.empty((H, nq), dtype=torch.float32, device=k_chunks[0].device))
     for i in units:
         o, l = outs[i]
         nq = q_chunks[i].shape[1]
@@ -401,9 +421,10 @@ def ring_backward_chunks(q_chunks, k_chunks, v_chunks, pos, mask: Mask, lses, de
     n_ranks = NC // C
     d = q_chunks[0].shape[2]
     if grads is None:
-        grads = [(torch.zeros(q_chunks[i].shape, dtype=torch.float32, device=q_chunks[i].device),
-                  torch.zeros(k_chunks[i].shape, dtype=torch.float32, device=k_chunks[i].device),
-                  torch.zeros(v_chunks[i].shape, dtype=torch.float32, device=v_chunks[i].device)) for i in range(NC)]
+        with _on(stream):
+            grads = [(torch.zeros(q_chunks[i].shape, dtype=torch.float32, device=q_chunks[i].device),
+                      torch.zeros(k_chunks[i].shape, dtype=torch.float32, device=k_chunks[i].device),
+                      torch.zeros(v_chunks[i].shape, dtype=torch.float32, device=v_chunks[i].device)) for i in range(NC)]
     qd = (_Tensor * NC)(*[_desc(t, "q") for t in q_chunks])
     kd = (_Tensor * NC)(*[_desc(t, "k") for t in k_chunks])
     vd = (_Tensor * NC)(*[_desc(t, "v") for t in v_chunks])
@@ -439,7 +460,8 @@ def merge_backward(parts, merged, g_o, g_lse=None, outs=None, stream=None):
         _f32_dev(po, "o_p")
         _f32_dev(pl, "lse_p")
     if outs is None:
-        outs = [(torch.empty_like(o), torch.empty_like(lse)) for _ in parts]
+        with _on(stream):
+            outs = [(torch.empty_like(o), torch.empty_like(lse)) for _ in parts]
     n = len(parts)
     P = ctypes.c_void_p
     arr = lambda ts: (P * n)(*[t.data_ptr() for t in ts])
@@ -459,9 +481,10 @@ def sink_backward(o: torch.Tensor, lse: torch.Tensor, sink_logits: torch.Tensor,
         raise ValueError("sink_backward expects o [H, n, d], lse [H, n], sink_logits [H], g_o [H, n, d]")
     for t, name in ((o, "o"), (lse, "lse"), (sink_logits, "sink_logits"), (g_o, "g_o")):
         _f32_dev(t, name)
-    g_in = torch.empty_like(o)
-    gl_in = torch.empty_like(lse)
-    ga = torch.empty_like(sink_logits)
+    with _on(stream):
+        g_in = torch.empty_like(o)
+        gl_in = torch.empty_like(lse)
+        ga = torch.empty_like(sink_logits)
     _check(lib().cpattn_sink_backward(o.data_ptr(), lse.data_ptr(), sink_logits.data_ptr(), H, n, d,
                                       g_o.data_ptr(), g_in.data_ptr(), gl_in.data_ptr(), ga.data_ptr(),
                                       _stream(stream)))
@@ -481,7 +504,8 @@ def backward_delta(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Te
     if o.shape != (H, n, d):
         raise ValueError("o and dout shapes differ")
     if delta is None:
-        delta = torch.empty((H, n), dtype=torch.float32, device=dout.device)
+        with _on(stream):
+            delta = torch.empty((H, n), dtype=torch.float32, device=dout.device)
     dd = _desc(dout, "dout")
     _check(lib().cpattn_backward_delta(_f32_dev(o, "o"), ctypes.byref(dd), _f32_dev(delta, "delta"),
                                        _stream(stream)))
@@ -496,9 +520,10 @@ def partial_backward(q, k, v, mask: Mask, lse, delta, dout, q_pos=(0, 1), k_pos=
     H, nq, d = q.shape
     Hk, nk, _ = k.shape
     if grads is None:
-        grads = (torch.zeros((H, nq, d), dtype=torch.float32, device=q.device),
-                 torch.zeros((Hk, nk, d), dtype=torch.float32, device=q.device),
-                 torch.zeros((Hk, nk, d), dtype=torch.float32, device=q.device))
+        with _on(stream):
+            grads = (torch.zeros((H, nq, d), dtype=torch.float32, device=q.device),
+                     torch.zeros((Hk, nk, d), dtype=torch.float32, device=q.device),
+                     torch.zeros((Hk, nk, d), dtype=torch.float32, device=q.device))
     dq, dk, dv = grads
     qd, kd, vd, dd = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(dout, "dout")
     _check(lib().cpattn_partial_backward(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), mask.handle,
@@ -519,9 +544,10 @@ def ring_backward(q_blocks, k_blocks, v_blocks, pos, mask: Mask, lses, deltas, d
     N = len(k_blocks)
     d = q_blocks[0].shape[2]
     if grads is None:
-        grads = [(torch.zeros(q_blocks[r].shape, dtype=torch.float32, device=q_blocks[r].device),
-                  torch.zeros(k_blocks[r].shape, dtype=torch.float32, device=k_blocks[r].device),
-                  torch.zeros(v_blocks[r].shape, dtype=torch.float32, device=v_blocks[r].device)) for r in range(N)]
+        with _on(stream):
+            grads = [(torch.zeros(q_blocks[r].shape, dtype=torch.float32, device=q_blocks[r].device),
+                      torch.zeros(k_blocks[r].shape, dtype=torch.float32, device=k_blocks[r].device),
+                      torch.zeros(v_blocks[r].shape, dtype=torch.float32, device=v_blocks[r].device)) for r in range(N)]
     qd = (_Tensor * N)(*[_desc(t, "q") for t in q_blocks])
     kd = (_Tensor * N)(*[_desc(t, "k") for t in k_blocks])
     vd = (_Tensor * N)(*[_desc(t, "v") for t in v_blocks])

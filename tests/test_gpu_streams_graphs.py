@@ -132,9 +132,9 @@ def test_backward_two_streams_and_graph_replay(cp):
     ref_b = cp.ring_backward(*B[:5], lb, db, gb, grads=zb(), stream=cur)
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    out_a, out_b = za(), zb()   # zero-filled on cur, before the side streams wait for it
     s1.wait_stream(cur)
     s2.wait_stream(cur)
-    out_a, out_b = za(), zb()
     cp.ring_backward(*A[:5], la, da, ga, grads=out_a, stream=s1)
     cp.ring_backward(*B[:5], lb, db, gb, grads=out_b, stream=s2)
     torch.cuda.synchronize()
@@ -161,3 +161,64 @@ def test_backward_two_streams_and_graph_replay(cp):
     del graph
     A[4].free()
     B[4].free()
+
+
+def test_two_host_threads_share_a_descriptor(cp):
+    """Two host threads (the binding's foreign calls release the interpreter
+    lock, so the library's host code runs in both at once) drive the forward
+    and backward rings of two problems through one windowed tree
+    descriptor, created just before, so that both fill its cached pair
+    counts together, each thread on its own stream, three times over: bit
+    for bit what each gives alone."""
+    import threading
+    seg, parent = workloads.tree_prompt_completions(2048, (1024,) * 3)
+    N = 4
+    n = len(seg)
+    c = n // N
+    dev = torch.device("cuda:0")
+    pos = [(r * c, 1) for r in range(N)]
+    blk = lambda t: [t[:, r * c:(r + 1) * c] for r in range(N)]
+    probs = []
+    for seed in (41, 42):
+        q, k, v = workloads.qkv(seed, 8, n, 128, "bf16")
+        G = torch.randn((8, n, 128), generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+        probs.append(tuple(blk(t.to(dev)) for t in (q, k, v)) + ([x.contiguous() for x in blk(G.to(dev))],))
+
+    def run(p, mask, stream):
+        Q, K, V, Gs = p
+        out = cp.ring_emulate(Q, K, V, pos, mask, stream=stream)
+        deltas = [cp.backward_delta(out[r][0], Gs[r], stream=stream) for r in range(N)]
+        grads = cp.ring_backward(Q, K, V, pos, mask, [out[r][1] for r in range(N)], deltas, Gs, stream=stream)
+        return out, grads
+
+    base = cp.Mask.tree(seg, parent)
+    ref_mask = base.with_window(700)
+    cur = torch.cuda.current_stream()
+    refs = [run(p, ref_mask, cur) for p in probs]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        mask = base.with_window(700)   # fresh: no cached pair counts yet
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for s in streams:
+            s.wait_stream(cur)
+        results, errors = [None, None], []
+
+        def worker(i):
+            try:
+                results[i] = run(probs[i], mask, streams[i])
+            except Exception as e:   # reported in the main thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        torch.cuda.synchronize()
+        assert not errors, errors
+        for i in range(2):
+            _same(results[i][0], refs[i][0], "thread %d forward, round %d" % (i, rep))
+            _same_grads(results[i][1], refs[i][1], "thread %d backward, round %d" % (i, rep))
+        mask.free()
+    ref_mask.free()
+    base.free()
