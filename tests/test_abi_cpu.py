@@ -218,3 +218,44 @@ def test_backward_validation(L):
     t7 = _tensor(cp, dtype=7)
     assert L.cpattn_backward_delta(0x2000, ctypes.byref(t7), 0x3000, None) == EUNSUPPORTED
     assert L.cpattn_mask_free(h) == OK
+
+
+def test_last_error_is_per_thread(L):
+    """cpattn_last_error() is the calling thread's own: eight host threads
+    fail validation at once, each in its own way, many times over, and each
+    reads back the message of its own failure (the binding's foreign calls
+    release the interpreter lock, so the calls do overlap)."""
+    import threading
+    import context_blockwise_attention_amd as cp
+    h = ctypes.c_void_p()
+    assert L.cpattn_mask_causal(64, ctypes.byref(h)) == OK
+    t = _tensor(cp)
+    cases = [
+        (lambda: _partial(L, cp, _tensor(cp, d=96), t, t, h), EUNSUPPORTED, b"head dim"),
+        (lambda: _partial(L, cp, t, t, t, h, scale=0.0), EUNSUPPORTED, b"scale"),
+        (lambda: _partial(L, cp, t, t, t, h, acc=2), EINVAL, b"accumulate"),
+        (lambda: _partial(L, cp, t, t, t, h, qpos=(60, 1)), EINVAL, b"q_pos"),
+        (lambda: _partial(L, cp, t, t, _tensor(cp, n=15), h), EINVAL, b"token counts"),
+        (lambda: _partial(L, cp, _tensor(cp, st=132), t, t, h), EUNSUPPORTED, b"strides"),
+        (lambda: _partial(L, cp, t, t, t, None), EINVAL, b"mask is NULL"),
+        (lambda: _partial(L, cp, t, t, t, h, o=0x2004), EUNSUPPORTED, b"aligned"),
+    ]
+    bad = []
+    start = threading.Barrier(len(cases))
+
+    def worker(call, code, word):
+        start.wait()
+        for _ in range(2000):
+            rc = call()
+            msg = L.cpattn_last_error()
+            if rc != code or word not in msg:
+                bad.append((word, rc, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert L.cpattn_mask_free(h) == OK
+    assert not bad, bad[:4]
