@@ -222,3 +222,57 @@ def test_two_host_threads_share_a_descriptor(cp):
         mask.free()
     ref_mask.free()
     base.free()
+
+
+def test_descriptors_made_in_several_threads(cp):
+    """Four host threads each build tree descriptors (and windowed copies of
+    them), run a ring through them on their own stream and free them, five
+    times over, all at once: every result bit for bit the one made alone."""
+    import threading
+    dev = torch.device("cuda:0")
+    shapes = [(700, (300, 450, 200)), (1024, (512,) * 4), (300, (900, 60)), (2048, (256,) * 6)]
+    windows = [0, 90, 400, 0]
+    N = 2
+    jobs = []
+    for i, (prompt, comps) in enumerate(shapes):
+        seg, parent = workloads.tree_prompt_completions(prompt, comps)
+        n = len(seg) // N * N
+        c = n // N
+        q, k, v = (t.to(dev) for t in workloads.qkv(50 + i, 4, n, 128, "bf16"))
+        blk = lambda t, c=c: [t[:, r * c:(r + 1) * c] for r in range(N)]
+        jobs.append((seg[:n], parent, windows[i], blk(q), blk(k), blk(v), [(r * c, 1) for r in range(N)]))
+
+    def run(job, stream):
+        seg, parent, w, Q, K, V, pos = job
+        base = cp.Mask.tree(seg, parent)
+        mask = base.with_window(w) if w else base
+        out = cp.ring_emulate(Q, K, V, pos, mask, stream=stream)
+        stream_sync = stream.synchronize if stream is not None else torch.cuda.synchronize
+        stream_sync()
+        if mask is not base:
+            mask.free()
+        base.free()
+        return out
+
+    refs = [run(j, None) for j in jobs]
+    results = [[None] * 5 for _ in jobs]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            for rep in range(5):
+                results[i][rep] = run(jobs[i], s)
+        except Exception as e:   # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(jobs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(jobs)):
+        for rep in range(5):
+            _same(results[i][rep], refs[i], "thread %d, round %d" % (i, rep))
