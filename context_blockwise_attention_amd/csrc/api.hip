@@ -1049,8 +1049,11 @@ extern "C" int cpattn_backward_delta(const float* o, const cpattn_tensor* dout, 
     if ((rc = check_tensor(dout, who, "dout"))) return rc;
     if (dout->n_tok == 0) return CPATTN_OK;
     if (!o || !delta) return fail(CPATTN_EINVAL, "%s: NULL pointer", who);
+    if ((reinterpret_cast<uintptr_t>(o) & 15) != 0 || (reinterpret_cast<uintptr_t>(delta) & 3) != 0)
+        return fail(CPATTN_EUNSUPPORTED, "%s: o must be 16-byte aligned and delta 4-byte aligned", who);
     const int64_t rows = dout->n_heads * dout->n_tok;
-    const int64_t blocks = (rows + 3) / 4;
+    const int64_t rows_per_block = 256 / (dout->d / 4);
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
     if (blocks > INT32_MAX) return fail(CPATTN_EUNSUPPORTED, "%s: too many rows", who);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (dout->dtype == CPATTN_BF16)

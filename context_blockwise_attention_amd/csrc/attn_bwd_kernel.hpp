@@ -532,21 +532,37 @@ __global__ void __launch_bounds__(kBwdThreads) attn_bwd_dkv_kernel(const BwdArgs
         }
 }
 
-// D = dot(dO, O) per query row (fp32), for one [H][n_q] block.
+// D = dot(dO, O) per query row (fp32), for one [H][n_q] block.  Each lane
+// takes 4 consecutive columns (16 bytes of O, 4 elements of dO), d / 4 lanes
+// share a row (a power of two dividing 64: 16 or 32) and reduce by shuffles,
+// 256 / (d / 4) rows per workgroup.  Both inputs are read once: non-temporal
+// loads.  O must be 16-byte aligned; dO's element offsets are multiples of 4
+// (its strides are multiples of 8 elements for bf16, 4 for fp32).
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(const float* o, const T* dout, int64_t do_sh, int32_t do_st,
                                                         float* delta, int64_t rows, int32_t n_q, int32_t d) {
-    // one wave per row
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const int64_t h = row / n_q, i = row % n_q;
+    using f4v = float __attribute__((ext_vector_type(4)));
+    using u2v = unsigned __attribute__((ext_vector_type(2)));
+    const int lanes = d >> 2;
+    const int64_t row = (int64_t)blockIdx.x * (256 / lanes) + threadIdx.x / lanes;
+    const int c = (threadIdx.x % lanes) * 4;
     float acc = 0.f;
-    for (int c = lane; c < d; c += 64)
-        acc += o[row * d + c] * (float)dout[h * do_sh + i * do_st + c];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) delta[row] = acc;
+    if (row < rows) {
+        const int64_t h = row / n_q, i = row - h * n_q;
+        const f4v ov = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(o + row * d + c));
+        const T* gp = dout + h * do_sh + i * do_st + c;
+        f4v gv;
+        if constexpr (sizeof(T) == 2) {
+            const u2v raw = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(gp));
+            gv = f4v{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+        } else {
+            gv = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(gp));
+        }
+        acc = ov.x * gv.x + ov.y * gv.y + ov.z * gv.z + ov.w * gv.w;
+    }
+    for (int off = lanes >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && threadIdx.x % lanes == 0) delta[row] = acc;
 }
 
 }  // namespace cpattn

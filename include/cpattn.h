@@ -263,8 +263,9 @@ int cpattn_apply_sink(float* o, float* lse, const float* sink_logits, int64_t n_
  * the forward (a key outside a query's window gets no gradient from it). */
 
 /* delta[h][i] = dot(dout[h][i][:], o[h][i][:]) for a complete output o
- * (fp32 [H][n][d], contiguous) and output gradient dout (bf16 or fp32, same
- * shape); delta: fp32 [H][n] device memory. */
+ * (fp32 [H][n][d], contiguous, 16-byte aligned) and output gradient dout
+ * (bf16 or fp32, same shape); delta: fp32 [H][n] device memory, 4-byte
+ * aligned.  EUNSUPPORTED for a misaligned o or delta. */
 int cpattn_backward_delta(const float* o, const cpattn_tensor* dout, float* delta, void* stream);
 
 /* Gradient contributions of one (query block, key/value block) pair, ADDED to

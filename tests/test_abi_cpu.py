@@ -217,6 +217,9 @@ def test_backward_validation(L):
                                      0x2000, None) == EINVAL                          # no mask
     t7 = _tensor(cp, dtype=7)
     assert L.cpattn_backward_delta(0x2000, ctypes.byref(t7), 0x3000, None) == EUNSUPPORTED
+    assert L.cpattn_backward_delta(0x2004, ctypes.byref(t), 0x3000, None) == EUNSUPPORTED   # o misaligned
+    assert L.cpattn_backward_delta(0x2000, ctypes.byref(t), 0x3002, None) == EUNSUPPORTED   # delta misaligned
+    assert L.cpattn_backward_delta(0, ctypes.byref(t), 0x3000, None) == EINVAL              # no o
     assert L.cpattn_mask_free(h) == OK
 
 
